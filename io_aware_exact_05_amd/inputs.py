@@ -1,0 +1,118 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module draws random numbers and rounds them to the storage dtype; it
+holds none of the attention arithmetic.  Both the GPU path and the CPU oracle
+consume what it produces, which is why it lives on its own.
+
+Recipe (every workload is synthetic; no dataset is involved):
+  * generator: numpy PCG64 seeded with ``SeedSequence([config_id, case_id])``
+    (ad-hoc shapes use ``SeedSequence([seed])``);
+  * draw fp64 standard normals for Q, then K, then V, each of shape
+    [B, H, N, d] in C order, then any outlier masks;
+  * outliers: the long-context workload scales round(0.01 N) distinct key rows
+    per (b, h) by 8 (peaked softmax rows); the fp8 workload multiplies each
+    entry of Q, K and V independently with probability 0.001 by 10;
+  * round once: fp64 -> fp32 (numpy, round-to-nearest-even), then fp32 -> the
+    storage dtype (torch, round-to-nearest-even).  The fp8 workload keeps the
+    fp32 values; quantising them is part of the method, not of the inputs.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+# Storage dtype names used across the package and the C ABI.
+TORCH_DTYPES = {
+    "f32": torch.float32,
+    "f16": torch.float16,
+    "bf16": torch.bfloat16,
+    "e4m3": torch.float32,  # unquantised fp32 values; quantised by the method
+}
+
+
+@dataclass(frozen=True)
+class Workload:
+    config_id: int
+    case_id: int
+    name: str
+    dtype: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: int
+    outliers: str = "none"  # "none" | "key_rows_x8" | "entries_x10"
+
+    @property
+    def scale(self) -> float:
+        """float32(1/sqrt(d)): the scale of the formula, as the caller passes it."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def flops(self) -> float:
+        """Metric FLOPs: 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def label(self) -> str:
+        c = "causal" if self.causal else "noncausal"
+        return (f"{self.name} B={self.B} H={self.H} N={self.N} d={self.d} "
+                f"{self.dtype} {c}")
+
+
+WORKLOADS = [
+    Workload(1, 0, "tiny_exact_f32", "f32", 1, 1, 128, 64, 0),
+    Workload(2, 0, "train_shape_bf16", "bf16", 4, 16, 2048, 128, 0),
+    Workload(2, 1, "train_shape_bf16", "bf16", 4, 16, 2048, 128, 1),
+    Workload(3, 0, "long_context_bf16", "bf16", 1, 32, 16384, 128, 1, "key_rows_x8"),
+    Workload(4, 0, "headdim_sweep_f16", "f16", 2, 16, 8192, 64, 1),
+    Workload(4, 1, "headdim_sweep_f16", "f16", 2, 16, 8192, 128, 1),
+    Workload(4, 2, "headdim_sweep_f16", "f16", 2, 16, 8192, 256, 1),
+    Workload(5, 0, "fp8_outliers", "e4m3", 4, 16, 4096, 128, 0, "entries_x10"),
+]
+
+
+def workload(config_id: int, case_id: int = 0) -> Workload:
+    for w in WORKLOADS:
+        if w.config_id == config_id and w.case_id == case_id:
+            return w
+    raise KeyError((config_id, case_id))
+
+
+def _round(x64: np.ndarray, dtype: str) -> torch.Tensor:
+    x32 = torch.from_numpy(np.ascontiguousarray(x64.astype(np.float32)))
+    return x32.to(TORCH_DTYPES[dtype])
+
+
+def draw(shape, dtype: str, seed_words, outliers: str = "none"):
+    """Q, K, V as CPU torch tensors of the storage dtype (fp32 for "e4m3")."""
+    B, H, N, d = shape
+    rng = np.random.default_rng(np.random.SeedSequence(list(seed_words)))
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    if outliers == "key_rows_x8":
+        n_rows = int(round(0.01 * N))
+        for b in range(B):
+            for h in range(H):
+                rows = rng.choice(N, size=n_rows, replace=False)
+                k[b, h, rows, :] *= 8.0
+    elif outliers == "entries_x10":
+        for x in (q, k, v):
+            mask = rng.random((B, H, N, d)) < 0.001
+            x[mask] *= 10.0
+    elif outliers != "none":
+        raise ValueError(outliers)
+    return _round(q, dtype), _round(k, dtype), _round(v, dtype)
+
+
+def workload_inputs(w: Workload):
+    return draw((w.B, w.H, w.N, w.d), w.dtype, (w.config_id, w.case_id), w.outliers)
+
+
+def random_inputs(B, H, N, d, dtype: str, seed: int, outliers: str = "none"):
+    """Ad-hoc shapes for parity and edge-case tests."""
+    return draw((B, H, N, d), dtype, (1000 + seed, B, H, N, d), outliers)

@@ -1,0 +1,6 @@
+"""fp64 CPU attention oracle — TEST INFRASTRUCTURE ONLY.
+
+Importable only from the tests, the smoke check and the benchmark's CPU
+baseline.  The GPU library must never depend on it.
+"""
+from .oracle import attention, attention_rows, build, load, num_threads  # noqa: F401
