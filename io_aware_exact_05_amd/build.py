@@ -1,0 +1,52 @@
+"""Build libfa.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+Usage: ``python -m io_aware_exact_05_amd.build``.  The library is written
+next to this file so that it travels with the source tree.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libfa.so")
+SOURCES = ["api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip"]
+ARCH = "gfx950"
+
+# Packed fp32 VALU forms are disabled: hipcc -O3 would otherwise form
+# v_pk_{add,mul,fma}_f32 from ordinary float code.
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def sources():
+    return [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    out_tmp = LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           *extra, *sources(), "-o", out_tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libfa.so")
+    noise = [ln for ln in (r.stdout + r.stderr).splitlines()
+             if ln.strip() and "packed-fp32-ops" not in ln]
+    if verbose and noise:
+        print("\n".join(noise))
+    os.replace(out_tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

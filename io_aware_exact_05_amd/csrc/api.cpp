@@ -1,0 +1,108 @@
+// C ABI of the attention forward pass: argument validation, dispatch to the
+// gfx950 kernels, launch-error mapping.  Declared in include/fa.h.
+//
+// Validation runs entirely on the host before any HIP call, so every invalid
+// argument is reported without touching (or needing) a device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int kAbiMajor = 1, kAbiMinor = 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, uint64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case FA_F32: return 4;
+    case FA_F16: return 2;
+    case FA_BF16: return 2;
+    case FA_E4M3: return 1;
+  }
+  return 0;
+}
+
+// Shape checks common to the entry points.  Sizes must index with 64-bit
+// offsets, B*H query tiles must fit one grid dimension, and one head must
+// stay below 2^31 elements (row offsets inside a head are 32-bit).
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+  const uint64_t bh = (uint64_t)B * (uint64_t)H;
+  if (bh > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  if ((uint64_t)N * (uint64_t)d > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  const uint64_t tiles = bh * (((uint64_t)N + 31) / 32);  // finest tiling used
+  if (tiles > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return (kAbiMajor << 16) | kAbiMinor; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N < 1, or the tensors are too large to index";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype not accepted by this entry point";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64, 128 or 256";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a tensor base pointer is misaligned";
+    case FA_ERR_ARG: return "FA_ERR_ARG: invalid option (causal, scale or similar)";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
+  }
+  return "unknown fa_status";
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int causal, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  const int sc = check_shape(B, H, N, d);
+  if (sc != FA_OK) return sc;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  const uint64_t rows = (uint64_t)B * H * N;
+  const uint64_t tbytes = rows * (uint64_t)d * elem_bytes(dtype);
+  const Range rq = range_of(q, tbytes), rk = range_of(k, tbytes), rv = range_of(v, tbytes);
+  const Range ro = range_of(o, tbytes), rl = range_of(lse, rows * 4);
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) ||
+      overlap(rl, rk) || overlap(rl, rv) || overlap(ro, rl))
+    return FA_ERR_ALIAS;
+
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = B * H;
+  p.N = N;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  hipError_t e = (dtype == FA_F32) ? fa::launch_fwd_f32(p, d, causal, s)
+                                   : fa::launch_fwd_half(p, d, causal, dtype == FA_BF16, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

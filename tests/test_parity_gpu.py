@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Small shapes compare every element and span several tiles plus a ragged tail;
+the full-size workloads run in the same launch configuration the benchmark
+times and compare sampled rows (first, last, tile-boundary and random rows of
+first, last and random heads), plus a finiteness check of every element.
+Gates: |O - O_ref| <= 1e-2 + half an output ulp of O_ref, |LSE - LSE_ref| <= 1e-3.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gates import check, widen
+from io_aware_exact_05_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def _fa():
+    from io_aware_exact_05_amd import fa
+    return fa
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(q, k, v, causal, scale):
+    fa = _fa()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, lse = fa.attention(qd, kd, vd, bool(causal), scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+SMALL_N = [1, 7, 64, 129, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("N", SMALL_N)
+@pytest.mark.parametrize("causal", [0, 1])
+def test_small_shapes_every_element(dtype, d, N, causal):
+    B, H = (1, 2) if N >= 1000 else (2, 3)
+    _say(f"case small dtype={dtype} d={d} N={N} causal={causal} B={B} H={H}")
+    q, k, v = inputs.random_inputs(B, H, N, d, dtype, seed=N + d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = run_gpu(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(widen(q), widen(k), widen(v), causal, scale)
+    st = check(o, lse, o_ref, lse_ref, dtype, f"{dtype} d={d} N={N} causal={causal}")
+    if dtype == "f32":  # fp32 operands and fp32 P: far inside the gate
+        assert st["o_max_abs"] < 1e-4 and st["lse_max_abs"] < 1e-4, st
+
+
+def _sample_rows(B, H, N, seed, per_head=24, heads=6):
+    rng = np.random.default_rng(seed)
+    hs = sorted(set([0, B * H - 1] + list(rng.integers(0, B * H, heads - 2))))
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, N // 2, N - 2, N - 1]
+    rows = []
+    for bh in hs:
+        rs = set(r for r in fixed if 0 <= r < N)
+        rs |= set(int(x) for x in rng.integers(0, N, per_head - len(rs)))
+        rows += [bh * N + r for r in sorted(rs)]
+    return np.array(rows, np.int64)
+
+
+FULL = [w for w in inputs.WORKLOADS if w.dtype != "e4m3"]
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: f"cfg{w.config_id}.{w.case_id}")
+def test_workload_full_size_sampled_rows(w):
+    _say(f"case workload {w.label()}")
+    q, k, v = inputs.workload_inputs(w)
+    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    rows = _sample_rows(w.B, w.H, w.N, seed=w.config_id * 10 + w.case_id)
+    if w.N <= 128 and w.B * w.H == 1:
+        rows = np.arange(w.N)
+    o_ref, lse_ref = oracle.attention_rows(widen(q), widen(k), widen(v), w.causal, w.scale, rows)
+    o_s = o.reshape(-1, w.d)[torch.from_numpy(rows)]
+    lse_s = lse.reshape(-1)[torch.from_numpy(rows)]
+    st = check(o_s, lse_s, o_ref, lse_ref, w.dtype, w.label())
+    _say(f"  {w.label()}: {st}")
+
+
+# ----------------------------- edge cases ---------------------------------
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1.5])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_unusual_scales(scale, causal):
+    _say(f"case scale={scale} causal={causal}")
+    q, k, v = inputs.random_inputs(1, 2, 300, 128, "bf16", seed=5)
+    o, lse = run_gpu(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(widen(q), widen(k), widen(v), causal, scale)
+    check(o, lse, o_ref, lse_ref, "bf16", f"scale={scale}")
+
+
+@pytest.mark.parametrize("BH", [(1, 8), (2, 8), (1, 9), (3, 5)])
+def test_head_counts_and_block_mapping(BH):
+    B, H = BH
+    _say(f"case B={B} H={H}")
+    for causal in (0, 1):
+        q, k, v = inputs.random_inputs(B, H, 260, 64, "f16", seed=B * 10 + H)
+        o, lse = run_gpu(q, k, v, causal, 0.125)
+        o_ref, lse_ref = oracle.attention(widen(q), widen(k), widen(v), causal, 0.125)
+        check(o, lse, o_ref, lse_ref, "f16", f"B={B} H={H} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_constant_v_gives_constant_output(causal):
+    _say(f"case constant V causal={causal}")
+    q, k, _ = inputs.random_inputs(2, 2, 200, 128, "bf16", seed=7)
+    c = torch.randn(2, 2, 1, 128).to(torch.bfloat16)
+    v = c.expand(2, 2, 200, 128).contiguous()
+    o, _ = run_gpu(q, k, v, causal, 0.09)
+    np.testing.assert_allclose(widen(o), np.broadcast_to(widen(c), o.shape), atol=1e-2, rtol=4e-3)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_identity_v_rows_of_p_sum_to_one(causal):
+    _say(f"case identity V causal={causal}")
+    N = d = 64
+    q, k, _ = inputs.random_inputs(1, 1, N, d, "f16", seed=9)
+    v = torch.eye(N, dtype=torch.float16).reshape(1, 1, N, d)
+    p, _ = run_gpu(q, k, v, causal, 0.3)
+    p = widen(p)[0, 0]
+    assert (p >= 0).all()
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-2)
+    if causal:
+        assert (p[np.triu(np.ones((N, N), bool), 1)] == 0).all()
+
+
+def test_deterministic_bitwise():
+    _say("case determinism")
+    q, k, v = inputs.random_inputs(2, 8, 700, 128, "bf16", seed=11)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    fa = _fa()
+    outs = []
+    for causal in (0, 1):
+        ref = None
+        for _ in range(3):
+            o, lse = fa.attention(qd, kd, vd, bool(causal), 0.088)
+            torch.cuda.synchronize()
+            if ref is None:
+                ref = (o.clone(), lse.clone())
+            else:
+                assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_every_output_written_and_no_out_of_bounds_writes(dtype):
+    _say(f"case poison/canary {dtype}")
+    B, H, N, d = 1, 3, 333, 128
+    q, k, v = inputs.random_inputs(B, H, N, d, dtype, seed=13)
+    fa = _fa()
+    n, guard = B * H * N * d, 4096
+    obuf = torch.full((n + 2 * guard,), float("nan"), dtype=TORCH[dtype], device="cuda")
+    lbuf = torch.full((B * H * N + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    obuf[:guard] = 7.0; obuf[-guard:] = 7.0
+    lbuf[:guard] = 7.0; lbuf[-guard:] = 7.0
+    o = obuf[guard:guard + n].view(B, H, N, d)
+    lse = lbuf[guard:guard + B * H * N].view(B, H, N)
+    for causal in (0, 1):
+        fa.fa_fwd(q.cuda(), k.cuda(), v.cuda(), o, lse, bool(causal), 0.088)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        assert (obuf[:guard] == 7).all() and (obuf[-guard:] == 7).all()
+        assert (lbuf[:guard] == 7).all() and (lbuf[-guard:] == 7).all()
+
+
+def test_status_errors_on_device_tensors():
+    _say("case error statuses")
+    fa = _fa()
+    q = torch.zeros(1, 1, 16, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FaError) as e:
+        fa.attention(q, q, q)
+    assert e.value.status == -4
+    q = torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 1, 16, device="cuda")
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd(q, q, q, q, lse, False, 0.1)  # o aliases the inputs
+    assert e.value.status == -7
