@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward pass on one MI355X.
+
+A step is one pass of the whole hot path over the training-shape workload
+(B=4, H=16, N=2048, d=128, bf16): the non-causal and the causal forward, the
+two cases that workload lists.  Inputs are seeded synthetic tensors resident
+in HBM before timing starts.  Prints ONE JSON line:
+
+  value        metric TFLOPS of the whole step: (4 B H N^2 d  +  half that for
+               the causal case) / time per step
+  roofline     the dominant kernel (the non-causal launch) against the bf16
+               dense MFMA peak, timed with HIP events on its own stream
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload,
+               on this host's cores
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --config C --case I     (another workload, same format)
+       python bench.py --profile-launches K    (only K non-causal launches; for
+                                                rocprofv3 runs)
+       python bench.py --copy-calib            (one 1 GiB device copy: the HBM
+                                                byte-counter calibration kernel)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_d128_B4H16N2048_noncausal_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_exact_05_amd", "csrc", f)
+                  for f in ("fa_fwd.hip", "fa_kernels.h")]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
+    when it is missing or was taken on a different kernel source."""
+    try:
+        txt = open(PROFILE_SUMMARY).read()
+    except OSError:
+        return None
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_sha():
+        return None
+    return float(m_b.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--case", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="CPU-baseline budget; the sample is sized to about this")
+    ap.add_argument("--profile-launches", type=int, default=0)
+    ap.add_argument("--copy-calib", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "every (batch, head) is independent, so N GPUs would each run B*H/N heads "
+              "with no communication — see the sharding paragraph of the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from io_aware_exact_05_amd import fa, inputs
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+
+    if args.copy_calib:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n}))
+        return
+
+    cases = [w for w in inputs.WORKLOADS if w.config_id == args.config
+             and (args.case is None or w.case_id == args.case)]
+    if not cases:
+        sys.exit(f"no workload config={args.config} case={args.case}")
+    if any(w.dtype == "e4m3" for w in cases):
+        sys.exit("the fp8 workload is not built into this benchmark yet")
+
+    data = []
+    for w in cases:
+        q, k, v = inputs.workload_inputs(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        data.append((w, (q, k, v), (qd, kd, vd, o, lse)))
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        w, _, (qd, kd, vd, o, lse) = data[i]
+        fa.fa_fwd(qd, kd, vd, o, lse, bool(w.causal), w.scale, stream)
+
+    if args.profile_launches:
+        for _ in range(args.profile_launches):
+            launch(0)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_launches": args.profile_launches, "workload": cases[0].label()}))
+        return
+
+    for _ in range(args.warmup):
+        for i in range(len(data)):
+            launch(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(data) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record(stream)
+        for i in range(len(data)):
+            launch(i)
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / K
+    per_case_ms = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)] for i in range(len(data))]
+    step_flops = sum(w.flops for w, _, _ in data)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    dtype = cases[0].dtype
+    peak = PEAK_TFLOPS[dtype]
+
+    case_rep = {}
+    for i, (w, _, _) in enumerate(data):
+        t = np.array(per_case_ms[i])
+        tf = w.flops / (np.median(t) * 1e-3) / 1e12
+        case_rep["causal" if w.causal else "noncausal"] = {
+            "ms_median": round(float(np.median(t)), 5), "ms_min": round(float(t.min()), 5),
+            "ms_p90": round(float(np.percentile(t, 90)), 5), "tflops": round(tf, 2),
+            "pct_of_peak": round(100 * tf / peak, 2)}
+
+    # dominant kernel: the one with the largest average launch time
+    avg = [float(np.mean(t)) for t in per_case_ms]
+    dom = int(np.argmax(avg))
+    wd = data[dom][0]
+    achieved = wd.flops / (avg[dom] * 1e-3) / 1e12
+    traffic = measured_traffic() if (wd.config_id, wd.case_id) == (2, 0) else None
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "kernel": f"fwd_mfma16 {wd.label()}", "avg_launch_ms": round(avg[dom], 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(data, args.cpu_seconds)
+
+    label = ", ".join(("causal" if w.causal else "noncausal") for w, _, _ in data)
+    w0 = cases[0]
+    out = {
+        "metric": "attention fwd TFLOPS (4*B*H*N^2*d, halved if causal) and % of MFMA peak, 1 GPU",
+        "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "pct_of_peak": round(100 * value / peak, 2),
+        "config": {"workload": f"{w0.name} ({label})", "B": w0.B, "H": w0.H, "N": w0.N,
+                   "d": w0.d, "causal": [w.causal for w, _, _ in data], "dtype": dtype,
+                   "step_flops": step_flops},
+        "cases": case_rep,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(data, budget_s):
+    """fp64 oracle on whole heads of the same workload, sized to ~budget_s."""
+    import numpy as np
+    import oracle
+
+    lib = oracle.load()
+    threads = oracle.num_threads(lib)
+    # pilot: one head of each case to estimate the rate
+    t_head = 0.0
+    for w, (q, k, v), _ in data:
+        q1, k1, v1 = (x[:1, :1].double().numpy() for x in (q, k, v))
+        t = time.perf_counter()
+        oracle.attention(q1, k1, v1, w.causal, w.scale, lib=lib)
+        t_head += time.perf_counter() - t
+    n_heads = data[0][0].B * data[0][0].H
+    take = int(max(1, min(n_heads, budget_s // max(t_head, 1e-6))))
+    flops = 0.0
+    t = time.perf_counter()
+    for w, (q, k, v), _ in data:
+        b_ = take // w.H
+        rem = take % w.H
+        parts = []
+        if b_:
+            parts.append(tuple(x[:b_].double().numpy() for x in (q, k, v)))
+        if rem:
+            parts.append(tuple(x[b_:b_ + 1, :rem].double().numpy() for x in (q, k, v)))
+        for qq, kk, vv in parts:
+            oracle.attention(qq, kk, vv, w.causal, w.scale, lib=lib)
+        flops += w.flops * take / n_heads
+    dt = time.perf_counter() - t
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{take} of {n_heads} heads (all {data[0][0].N} rows each) of every case "
+                      f"of the step, fp64, OpenMP over query rows"}
+
+
+if __name__ == "__main__":
+    main()
