@@ -2,12 +2,13 @@
 //
 // One workgroup owns BR = 128 query rows of one (batch, head): four wave64s,
 // each holding 32 rows for the whole pass.  The key/value sequence streams
-// through LDS in tiles of BC rows, double-buffered: the next tile's global
-// loads are issued before the current tile is consumed and land in the other
-// buffer afterwards, so one barrier per tile suffices ("FlashAttention (HI)",
-// tiling section: inputs split into tiles that fit on-chip memory, loaded in
-// turn, the final result updated; "FlashAttention-3 (BN)", memory-operations
-// section: the next block loads while the current one is computed).
+// through LDS in tiles of BC rows, double-buffered: the next tile's loads go
+// straight from HBM/L2 into the other LDS buffer (global_load_lds_dwordx4, no
+// staging registers) while the current tile is consumed, with one barrier
+// per tile ("FlashAttention (HI)", tiling section: inputs split into tiles
+// that fit on-chip memory, loaded in turn, the final result updated;
+// "FlashAttention-3 (BN)", memory-operations section: the next block loads
+// while the current one is computed).
 //
 // Per tile and wave (all on-chip; the score tile never reaches HBM):
 //   S^T = K_j Q^T   on v_mfma_f32_32x32x16_{bf16,f16}: keys on the MFMA rows,
@@ -18,11 +19,17 @@
 //                   scale folded into one FMA per score before v_exp_f32
 //                   ("FlashAttention (HI)", online-softmax section;
 //                   "FlashAttention-2 (BN)", fewer non-matmul operations).
+//                   m is only moved when a tile's max exceeds it by more than
+//                   2^8, so most tiles skip the O rescale; exp2(s - m) <= 256
+//                   then, and the result is the same softmax.
 //   O^T += V_j^T P^T  P stays in registers: the S^T accumulator layout is
 //                   exactly the B-operand layout of this MFMA once the key
 //                   order inside each 32-key block is permuted (bits 2 and 3 of
 //                   the row index swapped when K is read); V is read from LDS
 //                   already transposed with ds_read_b64_tr_b16.
+// LDS tiles are unpadded, 16-byte chunks XOR-swizzled per row so that both
+// the K operand reads (16 rows, one chunk column) and the transposed V reads
+// (4 rows x 4 chunks per half-wave) spread over all banks.
 // The epilogue divides by l once per row and writes O and the logsumexp once
 // ("FlashAttention (HI)", one-kernel section: only the final result is
 // written).
@@ -44,6 +51,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 
 typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_cvoid;
 
 // 16-bit element traits: the MFMA and the fp32 -> 16-bit packing (RNE).
 template <typename T> struct Half;
@@ -75,20 +84,45 @@ __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-__device__ __forceinline__ float wave_pair_max(float x) {
+// XOR swizzle of the 16-byte chunk index inside an LDS row.  Rows of 256 B
+// (d = 128) or 512 B (d = 256): the two 2-bit halves of row%16 are swapped, a
+// bijection of 0..15 whose values over any 4 consecutive rows differ in bits
+// 2-3.  Rows of 128 B (d = 64, two rows per 256-byte bank line): a map of
+// row%16 onto 0..7 that, paired with the row's half of the line, is again a
+// bijection, and differs in bit 2 between rows r and r+2.
+template <int D>
+__device__ __forceinline__ int chunk_swz(int row) {
+  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  else return ((row & 3) << 2) | ((row >> 2) & 3);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
   // lanes l and l^32 hold the same query: v_permlane32_swap exchanges halves.
   auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
                                             __builtin_bit_cast(unsigned, x), false, false);
   return fmaxf(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
 }
-__device__ __forceinline__ float wave_pair_sum(float x) {
+__device__ __forceinline__ float pair_sum(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
                                             __builtin_bit_cast(unsigned, x), false, false);
   return __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
 }
 
+// 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane i's
+// bytes land at LDS address lds_addr + 16 i; lds_addr must be wave-uniform.
+// Written as inline assembly so that the compiler does not tie every later
+// LDS read to this load's completion: the caller waits (s_waitcnt vmcnt(0))
+// and synchronises the workgroup before any wave reads the buffer.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kMInit = -1.0e30f;  // finite start of the running max
+constexpr float kLazy = 8.0f;       // log2 headroom before the running max moves
 
 // Block index -> (head, query tile).  Workgroups are dispatched round-robin
 // over the 8 XCDs (block b runs on XCD b % 8).  When the head count divides
@@ -109,19 +143,25 @@ __device__ __forceinline__ void decode_block(int bid, int BH, int nq, bool causa
   qt = causal ? nq - 1 - t : t;
 }
 
-template <typename T, int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_mfma16(FwdParams p) {
+template <int D> struct TileCfg;
+template <> struct TileCfg<64> { static constexpr int BC = 128, OCC = 2; };
+template <> struct TileCfg<128> { static constexpr int BC = 64, OCC = 2; };
+template <> struct TileCfg<256> { static constexpr int BC = 32, OCC = 1; };
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TileCfg<D>::OCC, TileCfg<D>::OCC)))
+void fwd_mfma16(FwdParams p) {
+  constexpr int BC = TileCfg<D>::BC;
   constexpr int NW = 4, BR = 32 * NW;
-  constexpr int KSTR = D + 8;    // K row stride in elements (+16 B)
-  constexpr int VSTR = D + 16;   // V row stride in elements (+32 B)
-  constexpr int KT = BC * KSTR, VT = BC * VSTR;
-  constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int CPT = BC * CPR / 256;     // chunks per thread per tensor
-  constexpr int NS = D / 16;              // MFMA k-steps of Q K^T
-  constexpr int NKB = BC / 32;            // 32-key blocks per tile
-  constexpr int ND = D / 32;              // 32-column blocks of O
-  static_assert(BC * CPR % 256 == 0, "tile must split evenly over 256 threads");
-  __shared__ __attribute__((aligned(16))) short smem[2 * (KT + VT)];
+  constexpr int RB = D * 2;                 // bytes per K/V row
+  constexpr int TB = BC * RB;               // bytes per K or V tile
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int CPT = BC * CPR / (64 * NW); // load instructions per wave per tensor
+  constexpr int NS = D / 16;                // MFMA k-steps of Q K^T
+  constexpr int NKB = BC / 32;              // 32-key blocks per tile
+  constexpr int ND = D / 32;                // 32-column blocks of O
+  static_assert(BC * CPR % (64 * NW) == 0, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];  // [stage][K,V]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
@@ -138,41 +178,63 @@ __global__ __launch_bounds__(256) void fwd_mfma16(FwdParams p) {
   const int myq = qrow0 + ql;          // this lane's query
 
   // Q operand (B of S^T = K Q^T): lane holds Q[myq][16 s + 8 g .. +8].
+  // Rows past the end read row N-1 (finite data; never stored).
   i32x4 qop[NS];
+  {
+    const T* qr = qh + (size_t)min(myq, N - 1) * D + 8 * g;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (myq < N) qop[s] = *(const i32x4*)(qh + (size_t)myq * D + 16 * s + 8 * g);
-    else qop[s] = i32x4{0, 0, 0, 0};
+    for (int s = 0; s < NS; ++s) qop[s] = *(const i32x4*)(qr + 16 * s);
+    // Consume the loads here: the tile copies below also count on vmcnt and
+    // the compiler does not see them, so no load of its own may stay pending
+    // into the loop (its waits would then also wait for the copies).
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qop[s]));
   }
 
   const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
   const int nt = (kv_end + BC - 1) / BC;
 
-  i32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int j) {
+  // ---- tile loader: wave w, instruction u fills LDS slots (u*NW + w)*64 + lane
+  // of a tile; slot -> (row, chunk), and the lane fetches the logical chunk
+  // that the swizzle stores there.  Rows past N re-read row N-1: finite values
+  // that the mask zeroes.
+  int ld_off[CPT];   // element offset of this lane's chunk within a tile
+  int ld_row[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int s = (u * NW + w) * 64 + lane, row = s / CPR, c = s % CPR;
+    ld_row[u] = row;
+    ld_off[u] = (c ^ chunk_swz<D>(row)) * 8;
+  }
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+  auto issue_tile = [&](int j, int stage) {
+    const uint32_t kdst = smem_base + stage * 2 * TB;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + 256 * u, row = c / CPR, col = c % CPR;
-      const int key = j * BC + row;
-      if (key < N) {
-        kreg[u] = *(const i32x4*)(kh + (size_t)key * D + col * 8);
-        vreg[u] = *(const i32x4*)(vh + (size_t)key * D + col * 8);
-      } else {
-        kreg[u] = i32x4{0, 0, 0, 0};
-        vreg[u] = i32x4{0, 0, 0, 0};
-      }
+      const size_t row = (size_t)min(j * BC + ld_row[u], N - 1);
+      const uint32_t lds_off = kdst + (u * NW + w) * 1024;
+      dma16(kh + row * D + ld_off[u], lds_off);
+      dma16(vh + row * D + ld_off[u], lds_off + TB);
     }
   };
-  auto swrite = [&](int st) {
-    short* sk = smem + st * (KT + VT);
-    short* sv = sk + KT;
+
+  // ---- per-lane LDS read geometry (byte offsets within a tile) ----
+  // K operand (A of S^T): row kb*32 + swap_bits23(ql), logical chunk 2 s + g.
+  const int krow = swap_bits23(ql);
+  const int kbase_off = krow * RB;
+  const int ky = g ^ chunk_swz<D>(krow);        // chunk(s) = (2 s) ^ ky
+  // V operand (A of O^T = V^T P^T), transposed read: in each 16-lane group,
+  // lane i points at row (i/4) and column 4*(i%4) of a 4 x 16 block; the
+  // hardware returns to lane i the 4 values of column i.  Rows kbase + trow
+  // (+4 for the second read), columns 32 b + 16 (lane/16 % 2) + 4 (i%4).
+  const int trow = (lane & 15) >> 2;
+  int vrow_off[2], vx[2];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + 256 * u, row = c / CPR, col = c % CPR;
-      *(i32x4*)(sk + row * KSTR + col * 8) = kreg[u];
-      *(i32x4*)(sv + row * VSTR + col * 8) = vreg[u];
-    }
-  };
+  for (int t = 0; t < 2; ++t) {
+    const int r = 8 * g + 4 * t + trow;  // row within the 16-key half block
+    vrow_off[t] = r * RB + 8 * (lane & 1);
+    vx[t] = (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ chunk_swz<D>(r);
+  }
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -184,48 +246,43 @@ __global__ __launch_bounds__(256) void fwd_mfma16(FwdParams p) {
   const float cabs = fabsf(c);
   const bool neg = c < 0.f;
 
-  // transposed-read geometry for the V operand (A of O^T = V^T P^T): in each
-  // 16-lane group, lane i points at row (i/4) and column 4*(i%4) of a 4 x 16
-  // block; the hardware returns to lane i the 4 values of column i.
-  const int trow = (lane & 15) >> 2;
-  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int krow = swap_bits23(ql);
-
-  gload(0);
-  swrite(0);
+  issue_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int j = 0; j < nt; ++j) {
     const int st = j & 1;
-    if (j + 1 < nt) gload(j + 1);
+    if (j + 1 < nt) issue_tile(j + 1, st ^ 1);
     const int key0 = j * BC;
     const bool active = !CAUSAL || key0 <= qrow0 + 31;
     if (active) {
-      const short* sk = smem + st * (KT + VT);
-      const short* sv = sk + KT;
+      const char* sk = smem + st * 2 * TB;
+      const char* sv = sk + TB;
       // ---- S^T = K_j Q^T ----
       f32x16 sacc[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        i32x4 kop[NS];
+        const char* kr = sk + kb * 32 * RB + kbase_off;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) kop[s] = *(const i32x4*)(kr + (((2 * s) ^ ky) << 4));
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-        const short* kr = sk + (kb * 32 + krow) * KSTR + 8 * g;
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-          sacc[kb] = Half<T>::mfma(*(const i32x4*)(kr + 16 * s), qop[s], sacc[kb]);
+        for (int s = 0; s < NS; ++s) sacc[kb] = Half<T>::mfma(kop[s], qop[s], sacc[kb]);
       }
       // ---- scale, mask, online softmax ----
       const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qrow0);
+      const int lim = CAUSAL ? min(myq, N - 1) : N - 1;  // last visible key
       // key of accumulator (kb, r) on this lane: key0 + 32 kb + 16 (r/8) + 8 g + r%8
       float mx = kNegInf;
       if (need_mask) {
-        const int lim = CAUSAL ? min(myq, N - 1) : N - 1;  // last visible key
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7);
-            float x = neg ? -sacc[kb][r] : sacc[kb][r];
+            const float x = neg ? -sacc[kb][r] : sacc[kb][r];
             mx = key <= lim ? fmaxf(mx, x) : mx;
           }
       } else {
@@ -234,15 +291,22 @@ __global__ __launch_bounds__(256) void fwd_mfma16(FwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, neg ? -sacc[kb][r] : sacc[kb][r]);
       }
-      mx = wave_pair_max(mx);
+      mx = pair_max(mx);
       const float mt = (mx == kNegInf) ? kNegInf : mx * cabs;
-      const float mnew = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      m = mnew;
-      const float negm = -mnew;
+      const bool upd = mt > m + kLazy;
+      if (__builtin_amdgcn_ballot_w64(upd)) {
+        const float mnew = upd ? mt : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < ND; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+      }
+      const float negm = -m;
       float rs = 0.f;
       if (need_mask) {
-        const int lim = CAUSAL ? min(myq, N - 1) : N - 1;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -263,11 +327,7 @@ __global__ __launch_bounds__(256) void fwd_mfma16(FwdParams p) {
             rs += pr;
           }
       }
-      l = l * alpha + rs;
-#pragma unroll
-      for (int b = 0; b < ND; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+      l += rs;
       // ---- O^T += V_j^T P^T ----
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -277,23 +337,29 @@ __global__ __launch_bounds__(256) void fwd_mfma16(FwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             pop[e] = (int)Half<T>::pack2(sacc[kb][8 * h + 2 * e], sacc[kb][8 * h + 2 * e + 1]);
-          const int kbase = kb * 32 + 16 * h + 8 * g;
+          const char* vb = sv + (kb * 32 + 16 * h) * RB;
+          i16x4 vlo[ND], vhi[ND];
 #pragma unroll
           for (int b = 0; b < ND; ++b) {
-            const short* vp = sv + (kbase + trow) * VSTR + 32 * b + tcol;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 4 * VSTR));
-            const i16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vb + vrow_off[0] + (((4 * b) ^ vx[0]) << 4)));
+            vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vb + vrow_off[1] + (((4 * b) ^ vx[1]) << 4)));
+          }
+#pragma unroll
+          for (int b = 0; b < ND; ++b) {
+            const i16x8 v8 = {vlo[b][0], vlo[b][1], vlo[b][2], vlo[b][3],
+                              vhi[b][0], vhi[b][1], vhi[b][2], vhi[b][3]};
             oacc[b] = Half<T>::mfma(__builtin_bit_cast(i32x4, v8), pop, oacc[b]);
           }
         }
     }
-    if (j + 1 < nt) swrite(st ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 (m + log2 l) ----
-  const float lt = wave_pair_sum(l);
+  const float lt = pair_sum(l);
   if (myq < N) {
     const float inv = 1.0f / lt;
     T* orow = (T*)p.o + head + (size_t)myq * D;
@@ -302,32 +368,32 @@ __global__ __launch_bounds__(256) void fwd_mfma16(FwdParams p) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         // registers 4a..4a+3 hold columns 32 b + 8 a + 4 g + 0..3
-        uint2 st;
-        st.x = Half<T>::pack2(oacc[b][4 * a] * inv, oacc[b][4 * a + 1] * inv);
-        st.y = Half<T>::pack2(oacc[b][4 * a + 2] * inv, oacc[b][4 * a + 3] * inv);
-        *(uint2*)(orow + 32 * b + 8 * a + 4 * g) = st;
+        uint2 stv;
+        stv.x = Half<T>::pack2(oacc[b][4 * a] * inv, oacc[b][4 * a + 1] * inv);
+        stv.y = Half<T>::pack2(oacc[b][4 * a + 2] * inv, oacc[b][4 * a + 3] * inv);
+        *(uint2*)(orow + 32 * b + 8 * a + 4 * g) = stv;
       }
     if (g == 0)
       p.lse[(size_t)bh * N + myq] = (m + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
   }
 }
 
-template <typename T, int D, int BC, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   constexpr int BR = 128;
   FwdParams q = p;
   q.nq = (p.N + BR - 1) / BR;
   const unsigned grid = (unsigned)(q.nq * p.BH);
-  hipLaunchKernelGGL((fwd_mfma16<T, D, BC, CAUSAL>), dim3(grid), dim3(256), 0, stream, q);
+  hipLaunchKernelGGL((fwd_mfma16<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, q);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_t(const FwdParams& p, int d, int causal, hipStream_t s) {
   switch (d) {
-    case 64:  return causal ? launch_one<T, 64, 64, true>(p, s) : launch_one<T, 64, 64, false>(p, s);
-    case 128: return causal ? launch_one<T, 128, 64, true>(p, s) : launch_one<T, 128, 64, false>(p, s);
-    case 256: return causal ? launch_one<T, 256, 32, true>(p, s) : launch_one<T, 256, 32, false>(p, s);
+    case 64:  return causal ? launch_one<T, 64, true>(p, s) : launch_one<T, 64, false>(p, s);
+    case 128: return causal ? launch_one<T, 128, true>(p, s) : launch_one<T, 128, false>(p, s);
+    case 256: return causal ? launch_one<T, 256, true>(p, s) : launch_one<T, 256, false>(p, s);
   }
   return hipErrorInvalidValue;
 }
