@@ -127,15 +127,22 @@ constexpr float kLazy = 8.0f;       // log2 headroom before the running max move
 // Block index -> (head, query tile).  Workgroups are dispatched round-robin
 // over the 8 XCDs (block b runs on XCD b % 8).  When the head count divides
 // by 8, each XCD gets a contiguous range of heads so that all query tiles of
-// a head share that XCD's L2 for K and V.  Within an XCD tiles go out in
-// tile-major order; for causal masking the heaviest (last) query tiles first.
+// a head share that XCD's L2 for K and V.  Without masking, an XCD runs its
+// heads one after another (the tiles of a head stream the same K/V tiles at
+// about the same time); with causal masking it goes tile-major, heaviest
+// (last) query tiles of every head first, for load balance.
 __device__ __forceinline__ void decode_block(int bid, int BH, int nq, bool causal,
                                              int& bh, int& qt) {
   int t;
   if ((BH & 7) == 0) {
     const int hx = BH >> 3, xcd = bid & 7, loc = bid >> 3;
-    t = loc / hx;
-    bh = xcd * hx + loc % hx;
+    if (causal) {  // tile-major: heavy tiles of every head first
+      t = loc / hx;
+      bh = xcd * hx + loc % hx;
+    } else {       // head-major: a head's tiles run together and share K/V in L2
+      t = loc % nq;
+      bh = xcd * hx + loc / nq;
+    }
   } else {
     t = bid / BH;
     bh = bid % BH;
@@ -143,10 +150,31 @@ __device__ __forceinline__ void decode_block(int bid, int BH, int nq, bool causa
   qt = causal ? nq - 1 - t : t;
 }
 
+// Key-tile rows BC and waves per SIMD (occupancy the register budget is cut
+// to) per head dimension.  The FA_D*_BC / FA_D*_OCC macros exist for tuning
+// builds only.
+#ifndef FA_D64_BC
+#define FA_D64_BC 128
+#endif
+#ifndef FA_D64_OCC
+#define FA_D64_OCC 2
+#endif
+#ifndef FA_D128_BC
+#define FA_D128_BC 64
+#endif
+#ifndef FA_D128_OCC
+#define FA_D128_OCC 2
+#endif
+#ifndef FA_D256_BC
+#define FA_D256_BC 32
+#endif
+#ifndef FA_D256_OCC
+#define FA_D256_OCC 1
+#endif
 template <int D> struct TileCfg;
-template <> struct TileCfg<64> { static constexpr int BC = 128, OCC = 2; };
-template <> struct TileCfg<128> { static constexpr int BC = 64, OCC = 2; };
-template <> struct TileCfg<256> { static constexpr int BC = 32, OCC = 1; };
+template <> struct TileCfg<64> { static constexpr int BC = FA_D64_BC, OCC = FA_D64_OCC; };
+template <> struct TileCfg<128> { static constexpr int BC = FA_D128_BC, OCC = FA_D128_OCC; };
+template <> struct TileCfg<256> { static constexpr int BC = FA_D256_BC, OCC = FA_D256_OCC; };
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TileCfg<D>::OCC, TileCfg<D>::OCC)))
@@ -189,6 +217,13 @@ void fwd_mfma16(FwdParams p) {
     // into the loop (its waits would then also wait for the copies).
 #pragma unroll
     for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qop[s]));
+    // A negative scale is moved into Q: scale*(q.k) = |scale|*((-q).k), and
+    // flipping the sign bit of a 16-bit float is exact.  The loop below then
+    // always sees a non-negative multiplier.
+    if (p.scale_log2 < 0.f) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qop[s] ^= (int)0x80008000u;
+    }
   }
 
   const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
@@ -242,9 +277,7 @@ void fwd_mfma16(FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float m = kMInit, l = 0.f;
-  const float c = p.scale_log2;
-  const float cabs = fabsf(c);
-  const bool neg = c < 0.f;
+  const float c = fabsf(p.scale_log2);  // >= 0; a negative sign went into Q
 
   issue_tile(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -260,6 +293,7 @@ void fwd_mfma16(FwdParams p) {
       const char* sv = sk + TB;
       // ---- S^T = K_j Q^T ----
       f32x16 sacc[NKB];
+      __builtin_amdgcn_s_setprio(1);  // MFMA phase: issue ahead of the other wave's softmax
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         i32x4 kop[NS];
@@ -271,6 +305,7 @@ void fwd_mfma16(FwdParams p) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) sacc[kb] = Half<T>::mfma(kop[s], qop[s], sacc[kb]);
       }
+      __builtin_amdgcn_s_setprio(0);
       // ---- scale, mask, online softmax ----
       const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qrow0);
       const int lim = CAUSAL ? min(myq, N - 1) : N - 1;  // last visible key
@@ -282,17 +317,16 @@ void fwd_mfma16(FwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7);
-            const float x = neg ? -sacc[kb][r] : sacc[kb][r];
-            mx = key <= lim ? fmaxf(mx, x) : mx;
+            mx = key <= lim ? fmaxf(mx, sacc[kb][r]) : mx;
           }
       } else {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, neg ? -sacc[kb][r] : sacc[kb][r]);
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
       }
       mx = pair_max(mx);
-      const float mt = (mx == kNegInf) ? kNegInf : mx * cabs;
+      const float mt = (mx == kNegInf) ? kNegInf : mx * c;
       const bool upd = mt > m + kLazy;
       if (__builtin_amdgcn_ballot_w64(upd)) {
         const float mnew = upd ? mt : m;
@@ -329,6 +363,7 @@ void fwd_mfma16(FwdParams p) {
       }
       l += rs;
       // ---- O^T += V_j^T P^T ----
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -353,6 +388,7 @@ void fwd_mfma16(FwdParams p) {
             oacc[b] = Half<T>::mfma(__builtin_bit_cast(i32x4, v8), pop, oacc[b]);
           }
         }
+      __builtin_amdgcn_s_setprio(0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();

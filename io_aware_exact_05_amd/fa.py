@@ -14,7 +14,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfa.so")
+# FA_LIB may name another build of the same library (tile-tuning builds).
+LIB_PATH = os.environ.get("FA_LIB") or os.path.join(_PKG, "libfa.so")
 
 # fa_dtype values
 FA_F32, FA_F16, FA_BF16, FA_E4M3 = 0, 1, 2, 3
