@@ -171,16 +171,59 @@ __device__ __forceinline__ void decode_block(int bid, int BH, int nq, bool causa
 #ifndef FA_D256_OCC
 #define FA_D256_OCC 1
 #endif
+#ifndef FA_D64_NW
+#define FA_D64_NW 4
+#endif
+#ifndef FA_D128_NW
+#define FA_D128_NW 8
+#endif
+#ifndef FA_D256_NW
+#define FA_D256_NW 4
+#endif
+#ifndef FA_D64_ST
+#define FA_D64_ST 2
+#endif
+#ifndef FA_D128_ST
+#define FA_D128_ST 4
+#endif
+#ifndef FA_D256_ST
+#define FA_D256_ST 4
+#endif
+// BC: key rows per tile; OCC: waves per SIMD the registers are budgeted
+// for; NW: waves per workgroup (32 query rows each); ST: LDS ring stages.
+// With two waves of the workgroup on each SIMD (NW = 8, OCC = 2) the upper
+// half of the workgroup runs half a tile behind the lower half ("ping-pong",
+// see the loop) and the ring prefetches ST - 2 tiles ahead, else ST - 1.
 template <int D> struct TileCfg;
-template <> struct TileCfg<64> { static constexpr int BC = FA_D64_BC, OCC = FA_D64_OCC; };
-template <> struct TileCfg<128> { static constexpr int BC = FA_D128_BC, OCC = FA_D128_OCC; };
-template <> struct TileCfg<256> { static constexpr int BC = FA_D256_BC, OCC = FA_D256_OCC; };
+template <> struct TileCfg<64> {
+  static constexpr int BC = FA_D64_BC, OCC = FA_D64_OCC, NW = FA_D64_NW, ST = FA_D64_ST;
+};
+template <> struct TileCfg<128> {
+  static constexpr int BC = FA_D128_BC, OCC = FA_D128_OCC, NW = FA_D128_NW, ST = FA_D128_ST;
+};
+template <> struct TileCfg<256> {
+  static constexpr int BC = FA_D256_BC, OCC = FA_D256_OCC, NW = FA_D256_NW, ST = FA_D256_ST;
+};
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 31] (the counter's immediate is
+// a compile-time field; gfx9 counts up to 63).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define FA_VMW(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    FA_VMW(0) FA_VMW(1) FA_VMW(2) FA_VMW(3) FA_VMW(4) FA_VMW(5) FA_VMW(6) FA_VMW(7)
+    FA_VMW(8) FA_VMW(9) FA_VMW(10) FA_VMW(11) FA_VMW(12) FA_VMW(13) FA_VMW(14) FA_VMW(15)
+    FA_VMW(16) FA_VMW(17) FA_VMW(18) FA_VMW(19) FA_VMW(20) FA_VMW(21) FA_VMW(22) FA_VMW(23)
+    FA_VMW(24) FA_VMW(25) FA_VMW(26) FA_VMW(27) FA_VMW(28) FA_VMW(29) FA_VMW(30) FA_VMW(31)
+#undef FA_VMW
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TileCfg<D>::OCC, TileCfg<D>::OCC)))
+__global__ __launch_bounds__(64 * TileCfg<D>::NW) __attribute__((amdgpu_waves_per_eu(TileCfg<D>::OCC, TileCfg<D>::OCC)))
 void fwd_mfma16(FwdParams p) {
   constexpr int BC = TileCfg<D>::BC;
-  constexpr int NW = 4, BR = 32 * NW;
+  constexpr int NW = TileCfg<D>::NW, BR = 32 * NW, ST = TileCfg<D>::ST;
   constexpr int RB = D * 2;                 // bytes per K/V row
   constexpr int TB = BC * RB;               // bytes per K or V tile
   constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -189,7 +232,11 @@ void fwd_mfma16(FwdParams p) {
   constexpr int NKB = BC / 32;              // 32-key blocks per tile
   constexpr int ND = D / 32;                // 32-column blocks of O
   static_assert(BC * CPR % (64 * NW) == 0, "tile must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];  // [stage][K,V]
+  constexpr bool PINGPONG = TileCfg<D>::OCC >= 2 && NW == 8;
+  constexpr int PD = PINGPONG ? ST - 2 : ST - 1;  // prefetch distance in tiles
+  static_assert(PD >= 1, "the ring is too short");
+  static_assert(2 * CPT * (PD - 1) <= 31, "pending copies must fit wait_vmcnt");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * 2 * TB];  // [stage][K,V]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
@@ -228,6 +275,9 @@ void fwd_mfma16(FwdParams p) {
 
   const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
   const int nt = (kv_end + BC - 1) / BC;
+  // Last tile this wave computes: with causal masking, tiles wholly above the
+  // wave's diagonal are skipped (the wave still helps copy them).
+  const int jlast = CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1;
 
   // ---- tile loader: wave w, instruction u fills LDS slots (u*NW + w)*64 + lane
   // of a tile; slot -> (row, chunk), and the lane fetches the logical chunk
@@ -277,121 +327,167 @@ void fwd_mfma16(FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float m = kMInit, l = 0.f;
-  const float c = fabsf(p.scale_log2);  // >= 0; a negative sign went into Q
+  // Multiplier of the scores in base 2.  A negative sign went into Q; a zero
+  // scale is raised to 1e-30, which moves no finite score's exponent by a
+  // representable amount but keeps -inf * c = -inf for hidden keys.
+  const float c = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
 
-  issue_tile(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // ---- the three per-tile steps ----
+  // S^T = K_j Q^T from LDS stage `st` into S.
+  auto qk = [&](int st, f32x16(&S)[NKB]) {
+    const char* sk = smem + st * 2 * TB;
+    __builtin_amdgcn_s_setprio(1);  // MFMA phase: issue ahead of the other wave's softmax
+    // K operands are read KPF MFMAs ahead of their use, so LDS latency hides
+    // behind the MFMA chain; the 32-key blocks' accumulation chains are
+    // interleaved (i % NKB is the block) so consecutive MFMAs are independent.
+    constexpr int NM = NKB * NS, KPF = NS;
+    i32x4 kop[NM];
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int kb = i % NKB, s = i / NKB;
+      kop[i] = *(const i32x4*)(sk + kb * 32 * RB + kbase_off + (((2 * s) ^ ky) << 4));
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) S[i % NKB] = Half<T>::mfma(kop[i], qop[i / NKB], S[i % NKB]);
+    __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);  // first KPF LDS reads
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (i + KPF < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next read
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-  for (int j = 0; j < nt; ++j) {
-    const int st = j & 1;
-    if (j + 1 < nt) issue_tile(j + 1, st ^ 1);
-    const int key0 = j * BC;
-    const bool active = !CAUSAL || key0 <= qrow0 + 31;
-    if (active) {
-      const char* sk = smem + st * 2 * TB;
-      const char* sv = sk + TB;
-      // ---- S^T = K_j Q^T ----
-      f32x16 sacc[NKB];
-      __builtin_amdgcn_s_setprio(1);  // MFMA phase: issue ahead of the other wave's softmax
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        i32x4 kop[NS];
-        const char* kr = sk + kb * 32 * RB + kbase_off;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) kop[s] = *(const i32x4*)(kr + (((2 * s) ^ ky) << 4));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) sacc[kb] = Half<T>::mfma(kop[s], qop[s], sacc[kb]);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // ---- scale, mask, online softmax ----
-      const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qrow0);
+  // Online-softmax update with the scores S of tile jj; S becomes P.
+  auto softmax = [&](int jj, f32x16(&S)[NKB]) {
+    const int key0 = jj * BC;
+    const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qrow0);
+    if (need_mask) {
+      // Accumulator (kb, r) of this lane holds key key0 + 8 g + kofs with
+      // kofs = 32 kb + 16 (r/8) + r%8 (a constant); it is visible iff
+      // kofs <= rel.  Hidden scores become -inf: the max ignores them and
+      // exp2 maps them to 0 (c > 0).
       const int lim = CAUSAL ? min(myq, N - 1) : N - 1;  // last visible key
-      // key of accumulator (kb, r) on this lane: key0 + 32 kb + 16 (r/8) + 8 g + r%8
-      float mx = kNegInf;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7);
-            mx = key <= lim ? fmaxf(mx, sacc[kb][r]) : mx;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      }
-      mx = pair_max(mx);
-      const float mt = (mx == kNegInf) ? kNegInf : mx * c;
-      const bool upd = mt > m + kLazy;
-      if (__builtin_amdgcn_ballot_w64(upd)) {
-        const float mnew = upd ? mt : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
-        l *= alpha;
-#pragma unroll
-        for (int b = 0; b < ND; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-      }
-      const float negm = -m;
-      float rs = 0.f;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7);
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, negm));
-            pr = key <= lim ? pr : 0.f;
-            sacc[kb][r] = pr;
-            rs += pr;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, negm));
-            sacc[kb][r] = pr;
-            rs += pr;
-          }
-      }
-      l += rs;
-      // ---- O^T += V_j^T P^T ----
-      __builtin_amdgcn_s_setprio(1);
+      const int rel = lim - key0 - 8 * g;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          i32x4 pop;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pop[e] = (int)Half<T>::pack2(sacc[kb][8 * h + 2 * e], sacc[kb][8 * h + 2 * e + 1]);
-          const char* vb = sv + (kb * 32 + 16 * h) * RB;
-          i16x4 vlo[ND], vhi[ND];
-#pragma unroll
-          for (int b = 0; b < ND; ++b) {
-            vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(vb + vrow_off[0] + (((4 * b) ^ vx[0]) << 4)));
-            vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(vb + vrow_off[1] + (((4 * b) ^ vx[1]) << 4)));
-          }
-#pragma unroll
-          for (int b = 0; b < ND; ++b) {
-            const i16x8 v8 = {vlo[b][0], vlo[b][1], vlo[b][2], vlo[b][3],
-                              vhi[b][0], vhi[b][1], vhi[b][2], vhi[b][3]};
-            oacc[b] = Half<T>::mfma(__builtin_bit_cast(i32x4, v8), pop, oacc[b]);
-          }
-        }
-      __builtin_amdgcn_s_setprio(0);
+        for (int r = 0; r < 16; ++r)
+          S[kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) <= rel) ? S[kb][r] : kNegInf;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Four independent partial maxima/sums keep the reduction chains short.
+    float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], S[kb][r]);
+    const float mx = pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
+    const float mt = (mx == kNegInf) ? kNegInf : mx * c;
+    const bool upd = mt > m + kLazy;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      const float mnew = upd ? mt : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < ND; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    }
+    const float negm = -m;
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, negm));
+        S[kb][r] = pr;
+        rs4[r & 3] += pr;
+      }
+    l += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+  };
+
+  // O^T += V^T P^T with V from LDS stage `st` and P in S.
+  auto pv = [&](int st, f32x16(&S)[NKB]) {
+    const char* sv = smem + st * 2 * TB + TB;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        i32x4 pop;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pop[e] = (int)Half<T>::pack2(S[kb][8 * h + 2 * e], S[kb][8 * h + 2 * e + 1]);
+        const char* vb = sv + (kb * 32 + 16 * h) * RB;
+        i16x4 vlo[ND], vhi[ND];
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+          vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vb + vrow_off[0] + (((4 * b) ^ vx[0]) << 4)));
+          vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vb + vrow_off[1] + (((4 * b) ^ vx[1]) << 4)));
+        }
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+          const i16x8 v8 = {vlo[b][0], vlo[b][1], vlo[b][2], vlo[b][3],
+                            vhi[b][0], vhi[b][1], vhi[b][2], vhi[b][3]};
+          oacc[b] = Half<T>::mfma(__builtin_bit_cast(i32x4, v8), pop, oacc[b]);
+        }
+      }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- ping-pong over key tiles ----
+  // The barrier at the end of every tile would otherwise put the two waves
+  // sharing a SIMD (waves w and w + 4: waves go round-robin over the four
+  // SIMDs of the CU) into the same phase, both on MFMAs or both on the
+  // softmax.  With PINGPONG the upper half of the workgroup therefore runs
+  // half a tile behind: in iteration j the lower half does QK_j, softmax_j,
+  // PV_j while the upper half does softmax_{j-1}, PV_{j-1}, QK_j, so one
+  // wave's exponentials overlap the other's matrix products.
+  //
+  // LDS ring of ST stages, prefetch distance PD: in iteration j tile j + PD
+  // is copied into the stage of tile j + PD - ST, which nobody reads any more
+  // (the lagging half finished PV_{j-2} before the last barrier); tile j + 1
+  // must have landed before the barrier that ends iteration j.  Each wave
+  // issues 2*CPT copies per tile and copies complete in order, so "tile j+1
+  // landed" is vmcnt <= 2*CPT * (tiles issued after it).
+  const bool lag = PINGPONG && w >= NW / 2;
+  for (int t = 0; t < PD && t < nt; ++t) issue_tile(t, t);
+  wait_vmcnt(2 * CPT * (min(nt, PD) - 1));
+  __syncthreads();
+
+  f32x16 sacc[NKB];
+  for (int j = 0; j < nt; ++j) {
+    if (j + PD < nt) issue_tile(j + PD, (j + PD) % ST);
+    if (!lag) {
+      if (j <= jlast) {
+        qk(j % ST, sacc);
+        softmax(j, sacc);
+        pv(j % ST, sacc);
+      }
+    } else {
+      if (j >= 1 && j - 1 <= jlast) {
+        softmax(j - 1, sacc);
+        pv((j - 1) % ST, sacc);
+      }
+      if (j <= jlast) qk(j % ST, sacc);
+    }
+    if (j + PD < nt) {  // steady state: tiles j+2 .. j+PD may stay in flight
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPT * (PD - 1)) : "memory");
+    } else {
+      wait_vmcnt(2 * CPT * max(0, nt - 1 - (j + 1)));
+    }
     __syncthreads();
+  }
+  if (lag && nt - 1 <= jlast) {  // the upper half's last tile (no copy can overwrite it now)
+    softmax(nt - 1, sacc);
+    pv((nt - 1) % ST, sacc);
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 (m + log2 l) ----
@@ -416,11 +512,11 @@ void fwd_mfma16(FwdParams p) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  constexpr int BR = 128;
+  constexpr int NW = TileCfg<D>::NW, BR = 32 * NW;
   FwdParams q = p;
   q.nq = (p.N + BR - 1) / BR;
   const unsigned grid = (unsigned)(q.nq * p.BH);
-  hipLaunchKernelGGL((fwd_mfma16<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, q);
+  hipLaunchKernelGGL((fwd_mfma16<T, D, CAUSAL>), dim3(grid), dim3(64 * NW), 0, stream, q);
   return hipGetLastError();
 }
 
