@@ -4,3 +4,4 @@ Importable only from the tests, the smoke check and the benchmark's CPU
 baseline.  The GPU library must never depend on it.
 """
 from .oracle import attention, attention_rows, build, load, num_threads  # noqa: F401
+from . import quant_oracle  # noqa: F401
