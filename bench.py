@@ -14,7 +14,11 @@ in HBM before timing starts.  Prints ONE JSON line:
                on this host's cores
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       python bench.py --config C --case I     (another workload, same format)
+       python bench.py --config C --case I     (another workload, same format;
+                                                the fp8 workload's step is the
+                                                three block quantisations, Q and K
+                                                rotated, then the fp8 attention;
+                                                the quantiser is reported apart)
        python bench.py --profile-launches K    (only K non-causal launches; for
                                                 rocprofv3 runs)
        python bench.py --copy-calib            (one 1 GiB device copy: the HBM
@@ -37,7 +41,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_d128_B4H16N2048_noncausal_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_exact_05_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_kernels.h")]
+                  for f in ("fa_fwd.hip", "fa_device.h", "fa_kernels.h")]
 
 
 def kernel_source_sha() -> str:
@@ -107,77 +111,110 @@ def main():
              and (args.case is None or w.case_id == args.case)]
     if not cases:
         sys.exit(f"no workload config={args.config} case={args.case}")
-    if any(w.dtype == "e4m3" for w in cases):
-        sys.exit("the fp8 workload is not built into this benchmark yet")
+    fp8 = cases[0].dtype == "e4m3"
+    stream = torch.cuda.current_stream()
 
-    data = []
+    # Each entry of `parts` is one launch of the step: (name, workload or None
+    # for a quantiser launch, callable).  Every buffer is allocated here.
+    data, parts = [], []
     for w in cases:
         q, k, v = inputs.workload_inputs(w)
         qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-        o = torch.empty_like(qd)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-        data.append((w, (q, k, v), (qd, kd, vd, o, lse)))
-    stream = torch.cuda.current_stream()
+        data.append((w, (q, k, v)))
+        if not fp8:
+            o = torch.empty_like(qd)
+            parts.append(("causal" if w.causal else "noncausal", w,
+                          lambda w=w, t=(qd, kd, vd, o, lse):
+                          fa.fa_fwd(*t, bool(w.causal), w.scale, stream)))
+            continue
+        signs = inputs.rotation_signs(w.d, seed=0).to(dev)
+        nblk = (w.N + 127) // 128
+        q8, k8, v8 = (torch.empty(qd.shape, dtype=torch.uint8, device=dev) for _ in range(3))
+        dq, dk, dv = (torch.empty((w.B, w.H, nblk), device=dev) for _ in range(3))
+        o = torch.empty(qd.shape, dtype=torch.bfloat16, device=dev)
+        for nm, x, x8, ds, rot in (("quantize_q", qd, q8, dq, 1), ("quantize_k", kd, k8, dk, 1),
+                                   ("quantize_v", vd, v8, dv, 0)):
+            parts.append((nm, None, lambda t=(x, x8, ds, rot):
+                          fa.fa_quantize_e4m3(t[0], t[1], t[2], t[3], signs if t[3] else None,
+                                              stream)))
+        parts.append(("attention_fp8", w, lambda w=w, t=(q8, k8, v8, dq, dk, dv, o, lse):
+                      fa.fa_fwd_fp8(*t, bool(w.causal), w.scale, stream)))
 
     def launch(i):
-        w, _, (qd, kd, vd, o, lse) = data[i]
-        fa.fa_fwd(qd, kd, vd, o, lse, bool(w.causal), w.scale, stream)
+        parts[i][2]()
 
     if args.profile_launches:
+        if fp8:
+            for i in range(len(parts) - 1):
+                launch(i)
+        att = [i for i, pt in enumerate(parts) if pt[1] is not None][0]
         for _ in range(args.profile_launches):
-            launch(0)
+            launch(att)
         torch.cuda.synchronize()
         print(json.dumps({"profile_launches": args.profile_launches, "workload": cases[0].label()}))
         return
 
     for _ in range(args.warmup):
-        for i in range(len(data)):
+        for i in range(len(parts)):
             launch(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(data) + 1)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         ev[s][0].record(stream)
-        for i in range(len(data)):
+        for i in range(len(parts)):
             launch(i)
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     ms_step = (t1 - t0) * 1e3 / K
-    per_case_ms = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)] for i in range(len(data))]
-    step_flops = sum(w.flops for w, _, _ in data)
+    per_part_ms = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)] for i in range(len(parts))]
+    step_flops = sum(w.flops for w, _ in data)
     value = step_flops / (ms_step * 1e-3) / 1e12
     dtype = cases[0].dtype
     peak = PEAK_TFLOPS[dtype]
 
     case_rep = {}
-    for i, (w, _, _) in enumerate(data):
-        t = np.array(per_case_ms[i])
-        tf = w.flops / (np.median(t) * 1e-3) / 1e12
-        case_rep["causal" if w.causal else "noncausal"] = {
-            "ms_median": round(float(np.median(t)), 5), "ms_min": round(float(t.min()), 5),
-            "ms_p90": round(float(np.percentile(t, 90)), 5), "tflops": round(tf, 2),
-            "pct_of_peak": round(100 * tf / peak, 2)}
+    for i, (nm, w, _) in enumerate(parts):
+        t = np.array(per_part_ms[i])
+        rep_i = {"ms_median": round(float(np.median(t)), 5), "ms_min": round(float(t.min()), 5),
+                 "ms_p90": round(float(np.percentile(t, 90)), 5)}
+        if w is not None:
+            tf = w.flops / (np.median(t) * 1e-3) / 1e12
+            rep_i.update(tflops=round(tf, 2), pct_of_peak=round(100 * tf / peak, 2))
+        else:  # quantiser: 4 bytes read and 1 written per element, plus the descales
+            w0 = cases[0]
+            nbytes = 5.0 * w0.B * w0.H * w0.N * w0.d + 4.0 * w0.B * w0.H * ((w0.N + 127) // 128)
+            rep_i.update(hbm_gbs=round(nbytes / (np.median(t) * 1e-3) / 1e9, 1),
+                         pct_of_hbm_peak=round(100 * nbytes / (np.median(t) * 1e-3) / 1e9
+                                               / HBM_PEAK_GBS, 2))
+        case_rep[nm] = rep_i
+    if fp8:
+        t_att = float(np.median(per_part_ms[-1]))
+        case_rep["attention_only_tflops"] = round(step_flops / (t_att * 1e-3) / 1e12, 2)
 
-    # dominant kernel: the one with the largest average launch time
-    avg = [float(np.mean(t)) for t in per_case_ms]
+    # dominant kernel: the attention launch with the largest average launch time
+    avg = [float(np.mean(t)) if parts[i][1] is not None else -1.0
+           for i, t in enumerate(per_part_ms)]
     dom = int(np.argmax(avg))
-    wd = data[dom][0]
+    wd = parts[dom][1]
     achieved = wd.flops / (avg[dom] * 1e-3) / 1e12
     traffic = measured_traffic() if (wd.config_id, wd.case_id) == (2, 0) else None
+    kname = "fwd_fp8" if fp8 else ("fwd_f32" if dtype == "f32" else "fwd_mfma16")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": f"fwd_mfma16 {wd.label()}", "avg_launch_ms": round(avg[dom], 5)}
+                "kernel": f"{kname} {wd.label()}", "avg_launch_ms": round(avg[dom], 5)}
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(data, args.cpu_seconds)
 
-    label = ", ".join(("causal" if w.causal else "noncausal") for w, _, _ in data)
+    label = ", ".join(("causal" if w.causal else "noncausal") for w, _ in data)
     w0 = cases[0]
     out = {
         "metric": "attention fwd TFLOPS (4*B*H*N^2*d, halved if causal) and % of MFMA peak, 1 GPU",
@@ -186,8 +223,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "pct_of_peak": round(100 * value / peak, 2),
         "config": {"workload": f"{w0.name} ({label})", "B": w0.B, "H": w0.H, "N": w0.N,
-                   "d": w0.d, "causal": [w.causal for w, _, _ in data], "dtype": dtype,
-                   "step_flops": step_flops},
+                   "d": w0.d, "causal": [w.causal for w, _ in data], "dtype": dtype,
+                   "step_flops": step_flops,
+                   **({"step": "quantise Q, K (rotated), V; fp8 attention"} if fp8 else {})},
         "cases": case_rep,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -204,7 +242,7 @@ def cpu_baseline(data, budget_s):
     threads = oracle.num_threads(lib)
     # pilot: one head of each case to estimate the rate
     t_head = 0.0
-    for w, (q, k, v), _ in data:
+    for w, (q, k, v) in data:
         q1, k1, v1 = (x[:1, :1].double().numpy() for x in (q, k, v))
         t = time.perf_counter()
         oracle.attention(q1, k1, v1, w.causal, w.scale, lib=lib)
@@ -213,7 +251,7 @@ def cpu_baseline(data, budget_s):
     take = int(max(1, min(n_heads, budget_s // max(t_head, 1e-6))))
     flops = 0.0
     t = time.perf_counter()
-    for w, (q, k, v), _ in data:
+    for w, (q, k, v) in data:
         b_ = take // w.H
         rem = take % w.H
         parts = []

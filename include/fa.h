@@ -69,6 +69,47 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, int causal, float scale, int dtype,
            void* stream);
 
+/*
+ * fa_fwd_fp8 — the same pass with OCP e4m3fn (finite-only, max 448) inputs,
+ * the 8-bit path of "FlashAttention-3 (BN)" / "(FA)" (sections on new
+ * hardware capabilities and on low precision).
+ *   q8, k8, v8          : [B,H,N,d] e4m3fn codes (one byte each).
+ *   q/k/v_descale        : fp32 [B,H,ceil(N/128)]; the value of element
+ *                          (b,h,i,c) is code * descale[b,h,i/128] (as written by
+ *                          fa_quantize_e4m3).  Each must be a positive
+ *                          normal fp32 value below 2^127 (not checked: they
+ *                          live in device memory; other values give
+ *                          unspecified output, never a fault).  Powers of two,
+ *                          as fa_quantize_e4m3 writes, are applied exactly.
+ *   o_bf16               : output [B,H,N,d] bfloat16.
+ *   lse                  : output [B,H,N] fp32, natural-log logsumexp of the
+ *                          scaled scores of the dequantised inputs.
+ *   causal, scale        : as in fa_fwd.  d must be 128 (else FA_ERR_HEADDIM).
+ * P is rounded to e4m3 for the second product; before rounding it is scaled
+ * by 2^6 (and by the non-power-of-two part of the V descale), which keeps it
+ * <= 256 (no saturation) and mostly above e4m3's subnormal range.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale,
+               const float* k_descale, const float* v_descale, void* o_bf16, float* lse,
+               int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * fa_quantize_e4m3 — fp32 [B,H,N,d] -> e4m3fn codes x8 [B,H,N,d] and fp32
+ * descale [B,H,ceil(N/block_rows)].  A block is block_rows (must be 128)
+ * consecutive rows of one (b,h) with all d columns.  The descale is the
+ * smallest power of two 2^e with amax <= 448 * 2^e (1 for an all-zero block)
+ * and code = e4m3(clamp(x * 2^-e, -448, 448)) rounded to nearest even; the
+ * power-of-two scaling is exact, so each code is a single rounding of
+ * x / descale (the reading of the pages' per-block fp32 scale used here).
+ *   rotate = 1 first applies x <- x H_d diag(signs) / sqrt(d) to every row
+ *   (H_d the Sylvester Hadamard matrix; signs: device float[d] of +-1, NULL =
+ *   all +1): the "incoherent processing" of the FlashAttention-3 pages, to be
+ *   applied with the same signs to Q and K and never to V.
+ * d in {64, 128, 256}.  x must not overlap x8 or descale.
+ */
+int fa_quantize_e4m3(const float* x, void* x8, float* descale, int B, int H, int N, int d,
+                     int block_rows, int rotate, const float* signs, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_string(int status);
 

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip"]
+SOURCES = ["api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_quant.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled: hipcc -O3 would otherwise form

@@ -105,4 +105,76 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale,
+               const float* k_descale, const float* v_descale, void* o_bf16, float* lse, int B,
+               int H, int N, int d, int causal, float scale, void* stream) {
+  if (!q8 || !k8 || !v8 || !q_descale || !k_descale || !v_descale || !o_bf16 || !lse)
+    return FA_ERR_NULL;
+  const int sc = check_shape(B, H, N, d);
+  if (sc != FA_OK) return sc;
+  if (d != 128) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o_bf16, 16) ||
+      !aligned(lse, 4) || !aligned(q_descale, 4) || !aligned(k_descale, 4) || !aligned(v_descale, 4))
+    return FA_ERR_ALIGN;
+  const uint64_t rows = (uint64_t)B * H * N;
+  const uint64_t nblk = ((uint64_t)N + 127) / 128;
+  const uint64_t dbytes = (uint64_t)B * H * nblk * 4;
+  const Range in[6] = {range_of(q8, rows * d), range_of(k8, rows * d), range_of(v8, rows * d),
+                       range_of(q_descale, dbytes), range_of(k_descale, dbytes),
+                       range_of(v_descale, dbytes)};
+  const Range ro = range_of(o_bf16, rows * d * 2), rl = range_of(lse, rows * 4);
+  for (const Range& r : in)
+    if (overlap(ro, r) || overlap(rl, r)) return FA_ERR_ALIAS;
+  if (overlap(ro, rl)) return FA_ERR_ALIAS;
+
+  fa::Fp8Params p{};
+  p.q = static_cast<const uint8_t*>(q8);
+  p.k = static_cast<const uint8_t*>(k8);
+  p.v = static_cast<const uint8_t*>(v8);
+  p.q_descale = q_descale;
+  p.k_descale = k_descale;
+  p.v_descale = v_descale;
+  p.o = o_bf16;
+  p.lse = lse;
+  p.BH = B * H;
+  p.N = N;
+  p.nblk = (int)nblk;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  (void)hipGetLastError();
+  const hipError_t e = fa::launch_fwd_fp8(p, d, causal, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_quantize_e4m3(const float* x, void* x8, float* descale, int B, int H, int N, int d,
+                     int block_rows, int rotate, const float* signs, void* stream) {
+  if (!x || !x8 || !descale) return FA_ERR_NULL;
+  const int sc = check_shape(B, H, N, d);
+  if (sc != FA_OK) return sc;
+  if (block_rows != 128 || (rotate != 0 && rotate != 1)) return FA_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(descale, 4) || (signs && !aligned(signs, 4)))
+    return FA_ERR_ALIGN;
+  const uint64_t elems = (uint64_t)B * H * N * d;
+  const uint64_t nblk = ((uint64_t)N + 127) / 128;
+  const Range rx = range_of(x, elems * 4), r8 = range_of(x8, elems),
+              rd = range_of(descale, (uint64_t)B * H * nblk * 4);
+  const Range rs = range_of(signs, signs ? (uint64_t)d * 4 : 0);
+  if (overlap(r8, rx) || overlap(rd, rx) || overlap(r8, rd) || overlap(r8, rs) || overlap(rd, rs))
+    return FA_ERR_ALIAS;
+  fa::QuantParams p{};
+  p.x = x;
+  p.x8 = static_cast<uint8_t*>(x8);
+  p.descale = descale;
+  p.BH = B * H;
+  p.N = N;
+  p.nblk = (int)nblk;
+  p.signs = rotate ? signs : nullptr;
+  p.inv_sqrt_d = (float)(1.0 / std::sqrt((double)d));
+  (void)hipGetLastError();
+  const hipError_t e =
+      fa::launch_quantize_e4m3(p, d, rotate, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -1,0 +1,97 @@
+// Device helpers shared by the attention kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+
+typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_cvoid;
+
+// Key held by MFMA row i of a 32-key block: bits 2 and 3 of i swapped.  The
+// map is its own inverse.  With it, accumulator register r of half-wave g
+// holds key 16*(r/8) + 8*g + (r%8): eight consecutive keys per register group.
+__device__ __forceinline__ int swap_bits23(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  // lanes l and l^32 hold the same query: v_permlane32_swap exchanges halves.
+  auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                            __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                            __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+}
+
+// 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane i's
+// bytes land at LDS address lds_addr + 16 i; lds_addr must be wave-uniform.
+// Written as inline assembly so that the compiler does not tie every later
+// LDS read to this load's completion: the caller waits (s_waitcnt vmcnt(0))
+// and synchronises the workgroup before any wave reads the buffer.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kMInit = -1.0e30f;  // finite start of the running max
+constexpr float kLazy = 8.0f;       // log2 headroom before the running max moves
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 31] (the counter's immediate is
+// a compile-time field; gfx9 counts up to 63).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define FA_VMW(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    FA_VMW(0) FA_VMW(1) FA_VMW(2) FA_VMW(3) FA_VMW(4) FA_VMW(5) FA_VMW(6) FA_VMW(7)
+    FA_VMW(8) FA_VMW(9) FA_VMW(10) FA_VMW(11) FA_VMW(12) FA_VMW(13) FA_VMW(14) FA_VMW(15)
+    FA_VMW(16) FA_VMW(17) FA_VMW(18) FA_VMW(19) FA_VMW(20) FA_VMW(21) FA_VMW(22) FA_VMW(23)
+    FA_VMW(24) FA_VMW(25) FA_VMW(26) FA_VMW(27) FA_VMW(28) FA_VMW(29) FA_VMW(30) FA_VMW(31)
+#undef FA_VMW
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// Block index -> (head, query tile).  Workgroups are dispatched round-robin
+// over the 8 XCDs (block b runs on XCD b % 8).  When the head count divides
+// by 8, each XCD gets a contiguous range of heads so that all query tiles of
+// a head share that XCD's L2 for K and V.  Without masking, an XCD runs its
+// heads one after another (the tiles of a head stream the same K/V tiles at
+// about the same time); with causal masking it goes tile-major, heaviest
+// (last) query tiles of every head first, for load balance.
+__device__ __forceinline__ void decode_block(int bid, int BH, int nq, bool causal,
+                                             int& bh, int& qt) {
+  int t;
+  if ((BH & 7) == 0) {
+    const int hx = BH >> 3, xcd = bid & 7, loc = bid >> 3;
+    if (causal) {  // tile-major: heavy tiles of every head first
+      t = loc / hx;
+      bh = xcd * hx + loc % hx;
+    } else {       // head-major: a head's tiles run together and share K/V in L2
+      t = loc % nq;
+      bh = xcd * hx + loc / nq;
+    }
+  } else {
+    t = bid / BH;
+    bh = bid % BH;
+  }
+  qt = causal ? nq - 1 - t : t;
+}
+
+}  // namespace fa

@@ -1,0 +1,313 @@
+// Fused exact attention forward with OCP e4m3 operands for gfx950.
+//
+// The fp8 variant of the method ("FlashAttention-3 (BN)" / "(FA)", sections
+// on new hardware capabilities and on low precision): both products run on
+// 8-bit floats, v_mfma_scale_f32_32x32x64_f8f6f4 at twice the bf16 rate, with
+// per-128-row fp32 descales for Q, K and V.
+//
+// Same tiling and online softmax as the 16-bit kernel: one workgroup owns
+// 128 query rows (four waves of 32), K/V tiles of 128 rows (one descale
+// block each) stream through a two-stage LDS ring filled by direct
+// global -> LDS copies; S^T = K8 Q8^T keeps one query per lane.
+//   scores    t = s8 * (scale log2 e * q_descale[query block] *
+//             k_descale[tile]): one per-tile multiplier folded into the FMA.
+//   V descale each tile's descale is split as v_descale = 2^e f with f in
+//             (1/2, 1]: 2^e enters the second product exactly as the MFMA's
+//             E8M0 block scale of the V^T operand, f is folded into P.  The
+//             block quantiser of this library emits powers of two (f = 1),
+//             for which the whole descale is applied without rounding.
+//   P         the rounded P that feeds the second product is
+//             P~ = e4m3(exp2(t - m + 8 - lazy + log2 f)).  The running max
+//             moves once a tile exceeds it by lazy = 2 (log2 units), so
+//             P = exp2(t - m) <= 4 and P~ <= 2^8 < 448 never saturates, while
+//             typical P~ stay well above e4m3's subnormal range (2^-6).  The
+//             running sum l counts the unrounded P (l += sum P~ 2^(lazy - 8)
+//             / f), and O = O~ 2^(lazy - 8) / l.
+//   P V       O^T += V8^T P~^T with V8 read transposed from LDS by
+//             ds_read_b64_tr_b8 (lane i of a 16-lane group receives byte
+//             i % 8 of the rows addressed by lanes 2e + i/8, e = 0..7).
+// Output O is bf16, the logsumexp fp32 in natural log.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef i32x2 __attribute__((address_space(3))) lds_i32x2;
+
+constexpr float kLazy8 = 2.0f;  // log2 headroom of the running max on this path
+
+// XOR swizzle of the 16-byte chunk inside a 128-byte fp8 row (two rows per
+// 256-byte bank line): for the K reads (16 rows, one chunk) every
+// (row parity, chunk) pair is distinct, and for the transposed V reads
+// (8 consecutive rows x 2 adjacent chunks per half-wave) so is every one of
+// the 16 (row, chunk) pairs.
+__device__ __forceinline__ int swz8(int row) { return (((row >> 1) & 3) << 1) | ((row >> 3) & 1); }
+
+__device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
+  // format 0 (e4m3) for both operands, E8M0 block scales 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Same product with A scaled by 2^(sa - 127) (sa an E8M0 biased exponent).
+__device__ __forceinline__ f32x16 mfma8_sa(i32x8 a, i32x8 b, f32x16 c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127);
+}
+
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  f32x2 v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_fp8(Fp8Params p) {
+  constexpr int D = 128, BC = 128, NW = 4, BR = 32 * NW, ST = 2;
+  constexpr int RB = D;                      // bytes per fp8 row
+  constexpr int TB = BC * RB;                // bytes per K or V tile
+  constexpr int SB = 2 * TB;                 // ring stage: K tile, then V tile
+  constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  constexpr int CPT = BC * CPR / (64 * NW);  // copies per wave per tile and tensor
+  constexpr int NS = D / 64;                 // MFMA k-steps of K Q^T
+  constexpr int NKB = BC / 32;               // 32-key blocks per tile
+  constexpr int NKS = BC / 64;               // MFMA k-steps of V^T P^T
+  constexpr int ND = D / 32;                 // 32-column blocks of O
+  static_assert(BC == 128 && BR == 128, "tiles coincide with the 128-row descale blocks");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * SB];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  int bh, qt;
+  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt);
+  const size_t head = (size_t)bh * N * D;
+  const uint8_t* __restrict__ qh = p.q + head;
+  const uint8_t* __restrict__ kh = p.k + head;
+  const uint8_t* __restrict__ vh = p.v + head;
+  const float* qd = p.q_descale + (size_t)bh * p.nblk;
+  const float* kd = p.k_descale + (size_t)bh * p.nblk;
+  const float* vd = p.v_descale + (size_t)bh * p.nblk;
+
+  const int qrow0 = qt * BR + w * 32;
+  const int myq = qrow0 + ql;
+
+  // Q operand (B of S^T = K Q^T): lane holds Q8[myq][64 s + 32 g .. +32].
+  // A negative scale is moved into Q (flip the e4m3 sign bits, exact).
+  i32x8 qop[NS];
+  {
+    const uint8_t* qr = qh + (size_t)min(myq, N - 1) * D + 32 * g;
+    const int flip = p.scale_log2 < 0.f ? (int)0x80808080u : 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const i32x4 lo = *(const i32x4*)(qr + 64 * s), hi = *(const i32x4*)(qr + 64 * s + 16);
+      qop[s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qop[s][e] ^= flip;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qop[s]));  // drain before the copies
+  }
+  const float c = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
+  const float cq = c * qd[qt];  // the workgroup's 128 rows are one descale block
+
+  const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
+  const int nt = (kv_end + BC - 1) / BC;
+  const int jlast = CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1;
+
+  // ---- copies (as in the 16-bit kernel, 128-byte rows) ----
+  int ld_row[CPT], ld_off[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int s = (u * NW + w) * 64 + lane, row = s / CPR, ch16 = s % CPR;
+    ld_row[u] = row;
+    ld_off[u] = (ch16 ^ swz8(row)) * 16;
+  }
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+  auto issue_tile = [&](int j, int stage) {
+    const uint32_t dst = smem_base + stage * SB + w * 1024;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const size_t row = (size_t)min(j * BC + ld_row[u], N - 1);
+      dma16(kh + row * D + ld_off[u], dst + u * NW * 1024);
+      dma16(vh + row * D + ld_off[u], dst + u * NW * 1024 + TB);
+    }
+  };
+
+  // K operand (A of S^T): row kb*32 + swap_bits23(ql), logical chunks
+  // 4 s + 2 g and 4 s + 2 g + 1.
+  const int krow = swap_bits23(ql);
+  const int kx = swz8(krow);
+  // V operand (A of O^T = V^T P~^T), transposed byte reads: lane r of each
+  // 16-lane group addresses row 32 kb + 16 h + 8 g + r/2, chunk 2 b + lane/16 % 2,
+  // byte 8 (r % 2) of that chunk.
+  const int tr = (lane & 15) >> 1;
+  const int vrow_off = (8 * g + tr) * RB + 8 * (lane & 1);
+  const int vx = ((lane >> 4) & 1) ^ swz8(8 * g + tr);
+
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int b = 0; b < ND; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
+  float m = kMInit, l = 0.f;
+
+  issue_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int j = 0; j < nt; ++j) {
+    const int st = j & 1;
+    if (j + 1 < nt) issue_tile(j + 1, st ^ 1);
+    if (j <= jlast) {
+      const char* sk = smem + st * SB;
+      const char* sv = sk + TB;
+      // ---- S^T = K8 Q8^T ----
+      f32x16 S[NKB];
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const char* kr = sk + (kb * 32 + krow) * RB;
+          const i32x4 lo = *(const i32x4*)(kr + (((4 * s + 2 * g) ^ kx) << 4));
+          const i32x4 hi = *(const i32x4*)(kr + (((4 * s + 2 * g + 1) ^ kx) << 4));
+          S[kb] = mfma8(i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, qop[s], S[kb]);
+        }
+      __builtin_amdgcn_s_setprio(0);
+      // ---- scale, mask, online softmax ----
+      const int key0 = j * BC;
+      const float ct = cq * kd[j];  // tile j is descale block j
+      if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qrow0)) {
+        const int lim = CAUSAL ? min(myq, N - 1) : N - 1;
+        const int rel = lim - key0 - 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            S[kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) <= rel) ? S[kb][r] : kNegInf;
+      }
+      float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], S[kb][r]);
+      const float mx = pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
+      const float mt = (mx == kNegInf) ? kNegInf : mx * ct;
+      const bool upd = mt > m + kLazy8;
+      if (__builtin_amdgcn_ballot_w64(upd)) {
+        const float mnew = upd ? mt : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < ND; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+      }
+      // v_descale = 2^e f, f in (1/2, 1]; the E8M0 scale 127 + e is kept in
+      // [0, 254] (255 encodes NaN)
+      const float vdj = vd[j];
+      int ex = __builtin_amdgcn_frexp_expf(vdj);
+      const float mant = __builtin_amdgcn_frexp_mantf(vdj);  // [1/2, 1)
+      const float f = (mant == 0.5f) ? 1.0f : mant;
+      ex -= (mant == 0.5f) ? 1 : 0;
+      const int sa = min(max(127 + ex, 0), 254);
+      const float beta = (8.0f - kLazy8) + __builtin_amdgcn_logf(f) - m;
+      const float lsc = __builtin_amdgcn_exp2f(kLazy8 - 8.0f) / f;
+      float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], ct, beta));
+          S[kb][r] = pr;
+          rs4[r & 3] += pr;
+        }
+      l += ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3])) * lsc;
+      // ---- O^T += V8^T P~^T ----
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        // P~ operand: bytes 16 kbh + 8 h + e <- S[2 ks + kbh][8 h + e]
+        i32x8 pop;
+#pragma unroll
+        for (int kbh = 0; kbh < 2; ++kbh)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q4 = 0; q4 < 2; ++q4) {
+              const f32x16& sv16 = S[2 * ks + kbh];
+              const int r0 = 8 * h + 4 * q4;
+              pop[4 * kbh + 2 * h + q4] =
+                  (int)pack4_e4m3(sv16[r0], sv16[r0 + 1], sv16[r0 + 2], sv16[r0 + 3]);
+            }
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+          i32x2 part[4];
+#pragma unroll
+          for (int kbh = 0; kbh < 2; ++kbh)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const char* a = sv + (32 * (2 * ks + kbh) + 16 * h) * RB + vrow_off +
+                              (((2 * b) ^ vx) << 4);
+              part[2 * kbh + h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
+            }
+          const i32x8 va = {part[0][0], part[0][1], part[1][0], part[1][1],
+                            part[2][0], part[2][1], part[3][0], part[3][1]};
+          oacc[b] = mfma8_sa(va, pop, oacc[b], sa);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O~ 2^(lazy - 8) / l, LSE = ln2 (m + log2 l) ----
+  const float lt = pair_sum(l);
+  if (myq < N) {
+    const float inv = __builtin_amdgcn_exp2f(kLazy8 - 8.0f) / lt;
+    __bf16* orow = (__bf16*)p.o + head + (size_t)myq * D;
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        uint2 stv;
+        stv.x = pack_bf16x2(oacc[b][4 * a] * inv, oacc[b][4 * a + 1] * inv);
+        stv.y = pack_bf16x2(oacc[b][4 * a + 2] * inv, oacc[b][4 * a + 3] * inv);
+        *(uint2*)(orow + 32 * b + 8 * a + 4 * g) = stv;
+      }
+    if (g == 0)
+      p.lse[(size_t)bh * N + myq] = (m + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, int causal, hipStream_t s) {
+  if (d != 128) return hipErrorInvalidValue;
+  Fp8Params q = p;
+  q.nq = (p.N + 127) / 128;
+  const unsigned grid = (unsigned)(q.nq * p.BH);
+  if (causal)
+    hipLaunchKernelGGL((fwd_fp8<true>), dim3(grid), dim3(256), 0, s, q);
+  else
+    hipLaunchKernelGGL((fwd_fp8<false>), dim3(grid), dim3(256), 0, s, q);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,6 +1,7 @@
 // Internal interface between the C ABI layer (api.cpp) and the kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -17,9 +18,44 @@ struct FwdParams {
   float scale_log2;  // scale * log2(e): scores go straight into exp2
 };
 
+// Arguments of the fp8 forward: q8/k8/v8 e4m3fn [B*H, N, d], per-128-row
+// fp32 descales [B*H, nblk], o bf16 [B*H, N, d], lse fp32 [B*H, N].
+struct Fp8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
+  void* o;
+  float* lse;
+  int BH;
+  int N;
+  int nq;            // query tiles per head (set by the launcher)
+  int nblk;          // 128-row descale blocks per head
+  float scale_log2;  // scale * log2(e)
+};
+
+// Arguments of the block quantiser: x fp32 [B*H, N, d] -> x8 e4m3fn, descale
+// fp32 [B*H, nblk]; optional rotation signs (NULL = all +1).
+struct QuantParams {
+  const float* x;
+  uint8_t* x8;
+  float* descale;
+  int BH;
+  int N;
+  int nblk;
+  const float* signs;
+  float inv_sqrt_d;
+};
+
 // fp16 / bf16 inputs, MFMA path.  d in {64, 128, 256}.
 hipError_t launch_fwd_half(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
 // fp32 inputs (v_mfma_f32_32x32x2f32).  d in {64, 128, 256}.
 hipError_t launch_fwd_f32(const FwdParams& p, int d, int causal, hipStream_t s);
+// e4m3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4).  d = 128.
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, int causal, hipStream_t s);
+// fp32 -> e4m3 block quantiser, optional randomised Hadamard rotation.
+hipError_t launch_quantize_e4m3(const QuantParams& p, int d, int rotate, hipStream_t s);
 
 }  // namespace fa

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_D
                 -7: "FA_ERR_ALIAS", -8: "FA_ERR_LAUNCH"}
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_status_string", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_quantize_e4m3", "fa_status_string", "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -44,6 +44,10 @@ def _load():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
+    lib.fa_quantize_e4m3.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp]
+    lib.fa_quantize_e4m3.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -113,4 +117,93 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# fp8 (OCP e4m3fn) path
+# ----------------------------------------------------------------------------
+
+def fa_fwd_fp8_raw(q8, k8, v8, qd, kd, vd, o, lse, B, H, N, d, causal, scale, stream=0) -> int:
+    """Direct call of fa_fwd_fp8 with integer pointers; returns the status."""
+    return int(_lib.fa_fwd_fp8(q8, k8, v8, qd, kd, vd, o, lse, int(B), int(H), int(N), int(d),
+                               int(causal), float(scale), stream))
+
+
+def fa_quantize_e4m3_raw(x, x8, descale, B, H, N, d, block_rows, rotate, signs, stream=0) -> int:
+    """Direct call of fa_quantize_e4m3 with integer pointers; returns the status."""
+    return int(_lib.fa_quantize_e4m3(x, x8, descale, int(B), int(H), int(N), int(d),
+                                     int(block_rows), int(rotate), signs, stream))
+
+
+def _dev(name, t, dtype=None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
+def fa_quantize_e4m3(x: torch.Tensor, x8: torch.Tensor, descale: torch.Tensor,
+                     rotate: bool = False, signs: torch.Tensor | None = None,
+                     stream=None) -> None:
+    """x fp32 [B,H,N,d] -> x8 (uint8 codes, same shape) and descale fp32 [B,H,ceil(N/128)]."""
+    _dev("x", x, torch.float32)
+    _dev("x8", x8, torch.uint8)
+    _dev("descale", descale, torch.float32)
+    if signs is not None:
+        _dev("signs", signs, torch.float32)
+    B, H, N, d = x.shape
+    if tuple(x8.shape) != (B, H, N, d) or tuple(descale.shape) != (B, H, (N + 127) // 128):
+        raise ValueError("x8 must match x and descale must be [B, H, ceil(N/128)]")
+    _check(fa_quantize_e4m3_raw(x.data_ptr(), x8.data_ptr(), descale.data_ptr(), B, H, N, d, 128,
+                                int(bool(rotate)), signs.data_ptr() if signs is not None else None,
+                                _stream_handle(stream)))
+
+
+def quantize_e4m3(x: torch.Tensor, rotate: bool = False, signs: torch.Tensor | None = None,
+                  stream=None):
+    """Allocate and quantise: returns (x8 uint8 [B,H,N,d], descale fp32 [B,H,ceil(N/128)])."""
+    B, H, N, d = x.shape
+    x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    desc = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
+    fa_quantize_e4m3(x, x8, desc, rotate, signs, stream)
+    return x8, desc
+
+
+def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, causal: bool, scale: float,
+               stream=None) -> None:
+    """fa_fwd_fp8 on device tensors: codes uint8 [B,H,N,d], descales fp32, o bf16, lse fp32."""
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _dev(name, t, torch.uint8)
+    for name, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
+        _dev(name, t, torch.float32)
+    _dev("o", o, torch.bfloat16)
+    _dev("lse", lse, torch.float32)
+    B, H, N, d = q8.shape
+    if k8.shape != q8.shape or v8.shape != q8.shape or o.shape != q8.shape:
+        raise ValueError("q8, k8, v8, o must share one [B, H, N, d] shape")
+    nb = (N + 127) // 128
+    for t in (q_descale, k_descale, v_descale):
+        if tuple(t.shape) != (B, H, nb):
+            raise ValueError("descales must be [B, H, ceil(N/128)]")
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    _check(fa_fwd_fp8_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_descale.data_ptr(),
+                          k_descale.data_ptr(), v_descale.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, int(bool(causal)), scale, _stream_handle(stream)))
+
+
+def attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                  scale: float | None = None, rotate: bool = True,
+                  signs: torch.Tensor | None = None, stream=None):
+    """fp32 Q, K, V -> quantise (Q and K rotated with the same signs when rotate) -> fp8
+    attention.  Returns (o bf16, lse fp32)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    q8, qd = quantize_e4m3(q, rotate, signs, stream)
+    k8, kd = quantize_e4m3(k, rotate, signs, stream)
+    v8, vd = quantize_e4m3(v, False, None, stream)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q8, k8, v8, qd, kd, vd, o, lse, causal, scale, stream)
     return o, lse

@@ -116,3 +116,9 @@ def workload_inputs(w: Workload):
 def random_inputs(B, H, N, d, dtype: str, seed: int, outliers: str = "none"):
     """Ad-hoc shapes for parity and edge-case tests."""
     return draw((B, H, N, d), dtype, (1000 + seed, B, H, N, d), outliers)
+
+
+def rotation_signs(d: int, seed: int = 0) -> torch.Tensor:
+    """The +-1 diagonal of the randomised Hadamard rotation (fp32, CPU)."""
+    rng = np.random.default_rng(np.random.SeedSequence([7777, seed, d]))
+    return torch.from_numpy(rng.choice(np.array([-1.0, 1.0], np.float32), d))

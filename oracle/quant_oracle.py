@@ -16,15 +16,19 @@ format definition:
   M M^T = I, so (Q M)(K M)^T = Q K^T.
 * Block quantisation (reading of the fp32 per-128-row scale): a block is 128
   consecutive sequence rows of one (b, h) with all d columns; amax is the
-  block's largest magnitude; descale = amax / 448 (fp32), codes =
-  e4m3_rne_saturate(x * (448 / amax)) with that product in fp32; an all-zero
+  block's largest magnitude; the descale is the smallest power of two
+  2^e with amax <= 448 * 2^e (an fp32 value), and codes =
+  e4m3_rne_saturate(x * 2^-e).  Scaling by a power of two is exact, so the
+  code is the single e4m3 rounding of x / descale, the block's largest
+  magnitude lands in [224, 448], and every later use of the scale (in fp32
+  arithmetic or as an MFMA power-of-two block scale) is exact.  An all-zero
   block gets descale 1 and zero codes.
 
-The fp32 steps follow the kernel's precision on purpose (a quantised code is
-an integer decided by floating point, so both sides decide it in fp32).  The
-rotation itself is computed here in fp64 from the matrix definition and
-rounded once to fp32, so rotated codes may differ from the GPU's by one code
-step where its fp32 butterflies round differently.
+Without rotation every step is exact up to the one e4m3 rounding, so codes
+and descales are bit-identical on any correct implementation.  The rotation
+is computed here in fp64 from the matrix definition and rounded once to
+fp32, so rotated codes may differ from a GPU's by one code step where its
+fp32 butterflies round differently.
 """
 from __future__ import annotations
 
@@ -98,6 +102,16 @@ def rotate(x, signs=None) -> np.ndarray:
     return (x @ rotation(x.shape[-1], signs)).astype(np.float32)
 
 
+def pow2_descale(amax) -> np.ndarray:
+    """Smallest power of two 2^e with amax <= 448 * 2^e (1 where amax == 0)."""
+    a = np.asarray(amax, dtype=np.float64)
+    e = np.ceil(np.log2(np.where(a > 0, a, 1.0) / E4M3_MAX))
+    # guard the floating-point log2 at exact powers: enforce the defining inequalities
+    e = np.where(a > E4M3_MAX * np.exp2(e), e + 1, e)
+    e = np.where(a <= E4M3_MAX * np.exp2(e - 1), e - 1, e)
+    return np.where(a > 0, np.exp2(e), 1.0).astype(np.float32)
+
+
 def quantize_blocks(x, block_rows: int = 128, rotate_signs=None, do_rotate: bool = False):
     """x fp32 [B, H, N, d] -> (codes uint8 [B,H,N,d], descale fp32 [B,H,ceil(N/block_rows)])."""
     x = np.asarray(x, dtype=np.float32)
@@ -108,13 +122,10 @@ def quantize_blocks(x, block_rows: int = 128, rotate_signs=None, do_rotate: bool
     codes = np.empty(x.shape, np.uint8)
     desc = np.empty((B, H, nb), np.float32)
     for i in range(nb):
-        blk = x[:, :, i * block_rows:(i + 1) * block_rows, :]
-        amax = np.abs(blk).max(axis=(2, 3)).astype(np.float32)
-        zero = amax == 0
-        inv = np.where(zero, np.float32(0), np.float32(E4M3_MAX) / np.where(zero, np.float32(1), amax))
-        desc[:, :, i] = np.where(zero, np.float32(1), amax / np.float32(E4M3_MAX))
-        y = (blk * inv.astype(np.float32)[:, :, None, None]).astype(np.float32)
-        y = np.clip(y, -E4M3_MAX, E4M3_MAX)
+        blk = x[:, :, i * block_rows:(i + 1) * block_rows, :].astype(np.float64)
+        ds = pow2_descale(np.abs(blk).max(axis=(2, 3)))
+        desc[:, :, i] = ds
+        y = np.clip(blk / ds.astype(np.float64)[:, :, None, None], -E4M3_MAX, E4M3_MAX)  # exact
         codes[:, :, i * block_rows:(i + 1) * block_rows, :] = e4m3_encode(y)
     return codes, desc
 

@@ -76,3 +76,51 @@ def test_inputs_may_alias_each_other():
     # itself is not attempted here, so only the alias rule is checked by
     # making another argument invalid afterwards.
     assert _call(k_ptr=Q, v_ptr=Q, causal=3) == -6
+
+
+# ---- fp8 entry points ----
+_NB = (N + 127) // 128
+QD, KD, VD = (0x20000000 + i * 0x100000 for i in range(3))
+FP8_OK = dict(q8=Q, k8=K, v8=V, qd=QD, kd=KD, vd=VD, o=O, lse=L, B=B, H=H, N=N, d=128,
+              causal=0, scale=0.088)
+
+
+def _fp8(**kw):
+    a = dict(FP8_OK)
+    a.update(kw)
+    return fa.fa_fwd_fp8_raw(**a)
+
+
+@pytest.mark.parametrize("which", ["q8", "k8", "v8", "qd", "kd", "vd", "o", "lse"])
+def test_fp8_null_pointer(which):
+    assert _fp8(**{which: 0}) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), -4), (dict(d=256), -4), (dict(d=100), -4), (dict(N=0), -2), (dict(H=0), -2),
+    (dict(causal=5), -6), (dict(scale=float("nan")), -6),
+    (dict(q8=Q + 4), -5), (dict(o=O + 2), -5), (dict(kd=KD + 2), -5),
+    (dict(o=Q), -7), (dict(lse=QD), -7), (dict(o=VD - 64), -7),
+])
+def test_fp8_invalid_arguments(kw, code):
+    assert _fp8(**kw) == code
+
+
+X, X8, DS, SG = (0x30000000 + i * 0x1000000 for i in range(4))
+QOK = dict(x=X, x8=X8, descale=DS, B=B, H=H, N=N, d=128, block_rows=128, rotate=1, signs=SG)
+
+
+def _qz(**kw):
+    a = dict(QOK)
+    a.update(kw)
+    return fa.fa_quantize_e4m3_raw(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), -1), (dict(x8=0), -1), (dict(descale=0), -1),
+    (dict(d=32), -4), (dict(N=0), -2), (dict(block_rows=64), -6), (dict(rotate=2), -6),
+    (dict(x=X + 4), -5), (dict(x8=X8 + 8), -5), (dict(descale=DS + 1), -5), (dict(signs=SG + 2), -5),
+    (dict(x8=X + 16), -7), (dict(descale=X8 + 4), -7), (dict(descale=SG), -7),
+])
+def test_quantize_invalid_arguments(kw, code):
+    assert _qz(**kw) == code

@@ -82,6 +82,15 @@ def test_hadamard_and_rotation_properties(d):
     np.testing.assert_allclose((q @ m) @ (k @ m).T, q @ k.T, atol=1e-12)
 
 
+def test_pow2_descale_definition():
+    amax = np.array([448.0, 448.0001, 224.0, 1.0, 3.5, 7.0, 1e-3, 0.0, 896.0, 895.9])
+    ds = qo.pow2_descale(amax)
+    np.testing.assert_array_equal(ds, [1.0, 2.0, 0.5, 2.0 ** -8, 2.0 ** -7, 2.0 ** -6, 2.0 ** -18,
+                                       1.0, 2.0, 2.0])
+    nz = amax > 0
+    assert (amax[nz] <= 448 * ds[nz]).all() and (amax[nz] > 224 * ds[nz]).all()
+
+
 def test_block_quantiser_identities():
     rng = np.random.default_rng(1)
     x = rng.standard_normal((1, 2, 300, 64)).astype(np.float32)
@@ -94,11 +103,13 @@ def test_block_quantiser_identities():
             blk = x[0, h, b * 128:(b + 1) * 128]
             if np.abs(blk).max() == 0:
                 continue
-            amax = np.float32(np.abs(blk).max())
-            assert desc[0, h, b] == np.float32(amax / np.float32(448))
-            # the largest element maps to (nearly) the top code
-            top = np.abs(qo.e4m3_decode(codes[0, h, b * 128:(b + 1) * 128])).max()
-            assert top == 448.0
+            amax = float(np.abs(blk).max())
+            ds = float(desc[0, h, b])
+            assert math.log2(ds) == round(math.log2(ds))          # a power of two
+            assert amax <= 448 * ds and amax > 224 * ds             # the smallest such
+            # codes are the single e4m3 rounding of x / descale
+            np.testing.assert_array_equal(codes[0, h, b * 128:(b + 1) * 128],
+                                          qo.e4m3_encode(blk.astype(np.float64) / ds))
     # dequantised values are within half a code step (relative 1/16) or the subnormal step
     deq = qo.dequantize_blocks(codes, desc)
     scale = np.repeat(desc, 128, axis=2)[:, :, :300, None]
