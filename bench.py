@@ -45,10 +45,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_exact_05_amd", "csrc", f)
 
 
 def kernel_source_sha() -> str:
+    """First 16 hex digits of the sha256 of the kernel sources with comments
+    and blank lines removed (edits to comments keep the measured kernel)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            txt = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in txt.splitlines())
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

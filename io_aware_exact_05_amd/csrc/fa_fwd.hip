@@ -1,14 +1,14 @@
 // Fused exact attention forward for gfx950 (MI355X), fp16/bf16 inputs.
 //
-// One workgroup owns BR = 128 query rows of one (batch, head): four wave64s,
-// each holding 32 rows for the whole pass.  The key/value sequence streams
-// through LDS in tiles of BC rows, double-buffered: the next tile's loads go
-// straight from HBM/L2 into the other LDS buffer (global_load_lds_dwordx4, no
-// staging registers) while the current tile is consumed, with one barrier
-// per tile ("FlashAttention (HI)", tiling section: inputs split into tiles
-// that fit on-chip memory, loaded in turn, the final result updated;
-// "FlashAttention-3 (BN)", memory-operations section: the next block loads
-// while the current one is computed).
+// One workgroup owns BR = 32 NW query rows of one (batch, head): NW wave64s
+// (8 at d = 128, 4 at d = 64 and 256), each holding 32 rows for the whole
+// pass.  The key/value sequence streams through LDS in tiles of BC rows, in a
+// ring of ST stages: later tiles' loads go straight from HBM/L2 into free
+// stages (global_load_lds_dwordx4, no staging registers) while the current
+// tile is consumed, with one barrier per tile ("FlashAttention (HI)", tiling
+// section: inputs split into tiles that fit on-chip memory, loaded in turn,
+// the final result updated; "FlashAttention-3 (BN)", memory-operations
+// section: the next block loads while the current one is computed).
 //
 // Per tile and wave (all on-chip; the score tile never reaches HBM):
 //   S^T = K_j Q^T   on v_mfma_f32_32x32x16_{bf16,f16}: keys on the MFMA rows,
