@@ -41,7 +41,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_d128_B4H16N2048_noncausal_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_exact_05_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_device.h", "fa_kernels.h")]
+                  for f in ("fa_fwd.hip", "fa_fwd_wide.hip", "fa_device.h", "fa_kernels.h")]
 
 
 def kernel_source_sha() -> str:
@@ -68,6 +68,17 @@ def measured_traffic():
     if not m_sha or not m_b or m_sha.group(1) != kernel_source_sha():
         return None
     return float(m_b.group(1))
+
+
+def kernel_name(w) -> str:
+    """The kernel the library dispatches for workload w (for labels only)."""
+    if w.dtype == "e4m3":
+        return "fwd_fp8"
+    if w.dtype == "f32":
+        return "fwd_f32"
+    if w.d == 128 and (not w.causal or (w.N + 255) // 256 * w.B * w.H > 512):
+        return "fwd_wide"
+    return "fwd_mfma16"
 
 
 def parse():
@@ -209,7 +220,7 @@ def main():
     wd = parts[dom][1]
     achieved = wd.flops / (avg[dom] * 1e-3) / 1e12
     traffic = measured_traffic() if (wd.config_id, wd.case_id) == (2, 0) else None
-    kname = "fwd_fp8" if fp8 else ("fwd_f32" if dtype == "f32" else "fwd_mfma16")
+    kname = kernel_name(wd)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": f"{kname} {wd.label()}", "avg_launch_ms": round(avg[dom], 5)}

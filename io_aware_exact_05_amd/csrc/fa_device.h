@@ -94,4 +94,39 @@ __device__ __forceinline__ void decode_block(int bid, int BH, int nq, bool causa
   qt = causal ? nq - 1 - t : t;
 }
 
+// 16-bit element traits: the MFMA and the fp32 -> 16-bit packing (RNE).
+template <typename T> struct Half;
+template <> struct Half<__bf16> {
+  static __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+};
+template <> struct Half<_Float16> {
+  static __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+};
+
+// XOR swizzle of the 16-byte chunk index inside an LDS row.  Rows of 256 B
+// (d = 128) or 512 B (d = 256): the two 2-bit halves of row%16 are swapped, a
+// bijection of 0..15 whose values over any 4 consecutive rows differ in bits
+// 2-3.  Rows of 128 B (d = 64, two rows per 256-byte bank line): a map of
+// row%16 onto 0..7 that, paired with the row's half of the line, is again a
+// bijection, and differs in bit 2 between rows r and r+2.
+template <int D>
+__device__ __forceinline__ int chunk_swz(int row) {
+  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  else return ((row & 3) << 2) | ((row >> 2) & 3);
+}
+
 }  // namespace fa

@@ -36,45 +36,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
-
-// 16-bit element traits: the MFMA and the fp32 -> 16-bit packing (RNE).
-template <typename T> struct Half;
-template <> struct Half<__bf16> {
-  static __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
-    f32x2 v = {x, y};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  }
-};
-template <> struct Half<_Float16> {
-  static __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
-    f32x2 v = {x, y};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  }
-};
-
-// XOR swizzle of the 16-byte chunk index inside an LDS row.  Rows of 256 B
-// (d = 128) or 512 B (d = 256): the two 2-bit halves of row%16 are swapped, a
-// bijection of 0..15 whose values over any 4 consecutive rows differ in bits
-// 2-3.  Rows of 128 B (d = 64, two rows per 256-byte bank line): a map of
-// row%16 onto 0..7 that, paired with the row's half of the line, is again a
-// bijection, and differs in bit 2 between rows r and r+2.
-template <int D>
-__device__ __forceinline__ int chunk_swz(int row) {
-  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  else return ((row & 3) << 2) | ((row >> 2) & 3);
-}
 
 // Key-tile rows BC and waves per SIMD (occupancy the register budget is cut
 // to) per head dimension.  The FA_D*_BC / FA_D*_OCC macros exist for tuning
@@ -96,6 +63,9 @@ __device__ __forceinline__ int chunk_swz(int row) {
 #endif
 #ifndef FA_D256_OCC
 #define FA_D256_OCC 1
+#endif
+#ifndef FA_D128_WIDE
+#define FA_D128_WIDE 1  // d = 128 runs fwd_wide (fa_fwd_wide.hip); 0 = the kernel below
 #endif
 #ifndef FA_D64_NW
 #define FA_D64_NW 4
@@ -432,11 +402,28 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Causal work per query tile grows with the tile index.  fwd_wide runs two
+// 256-row workgroups per CU; when its whole grid fits in one round of those
+// slots the heaviest tiles alone set the runtime, and fwd_mfma16 (one 8-wave
+// workgroup per CU, two rounds, heaviest tiles first) balances better.
+static bool causal_fills_several_rounds(const FwdParams& p) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const long long grid = (long long)((p.N + 255) / 256) * p.BH;
+  return grid > 2LL * cus;
+}
+
 template <typename T>
 static hipError_t launch_t(const FwdParams& p, int d, int causal, hipStream_t s) {
   switch (d) {
     case 64:  return causal ? launch_one<T, 64, true>(p, s) : launch_one<T, 64, false>(p, s);
-    case 128: return causal ? launch_one<T, 128, true>(p, s) : launch_one<T, 128, false>(p, s);
+    case 128:
+#if FA_D128_WIDE
+      if (!causal || causal_fills_several_rounds(p)) return launch_fwd_wide(p, causal, std::is_same<T, __bf16>::value, s);
+#endif
+      return causal ? launch_one<T, 128, true>(p, s) : launch_one<T, 128, false>(p, s);
     case 256: return causal ? launch_one<T, 256, true>(p, s) : launch_one<T, 256, false>(p, s);
   }
   return hipErrorInvalidValue;

@@ -1,0 +1,347 @@
+// Fused exact attention forward for gfx950, fp16/bf16 inputs, d = 128.
+//
+// The method is that of "FlashAttention (HI)" (tiling, online softmax, one
+// kernel writing only O and the logsumexp); the tile shapes are chosen for
+// CDNA4.  Each wave owns 64 query rows (two 32-row MFMA blocks) and streams
+// 32-key tiles of K and V through LDS:
+//   * every K or V operand read from LDS feeds two MFMAs (one per query
+//     block), half the LDS traffic per flop of a 32-row wave.  With 32 rows
+//     per wave the LDS reads of a tile, plus the copies filling it, take about
+//     as long as its MFMAs, and the two units cap each other;
+//   * the whole state (O 64 x 128 fp32, the score tile, Q) fits in 256
+//     VGPRs, so two workgroups share a CU and each SIMD runs two waves: while
+//     one computes exponentials the other issues matrix products.  MFMAs are
+//     built in VGPR form (compiler flag for this file), which keeps the
+//     accumulators out of the AGPRs and avoids copies between the two files.
+// Score layout, key permutation, transposed V reads, chunk swizzle, lazy
+// running max and masking follow fwd_mfma16 (fa_fwd.hip).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+// Raw buffer resource over [base, base + bytes) (stride 0; data format 32 bit,
+// the value the gfx9 family expects for untyped buffer loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16-byte buffer -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane i's
+// bytes land at LDS address lds_addr + 16 i.  An offset past the resource's
+// size reads zeros instead of memory.  Inline assembly for the same reason
+// as dma16: the caller does its own vmcnt accounting.
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_wide(FwdParams p) {
+  constexpr int D = 128, BC = 32, NW = 4, QB = 2, WR = 32 * QB, BR = WR * NW, ST = 4;
+  constexpr int RB = D * 2;                  // bytes per K/V row
+  constexpr int TB = BC * RB;                // bytes per K or V tile (8 KiB)
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int CPT = BC * CPR / (64 * NW);  // copies per wave per tile and tensor
+  constexpr int NS = D / 16;                 // MFMA k-steps of K Q^T
+  constexpr int NKB = BC / 32;               // 32-key blocks per tile
+  constexpr int ND = D / 32;                 // 32-column blocks of O
+  static_assert(CPT * 64 * NW == BC * CPR, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * 2 * TB];  // [stage][K, V], 64 KiB
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int ql = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  int bh, qt;
+  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt);
+
+  const size_t head = (size_t)bh * N * D;
+  const T* __restrict__ qh = (const T*)p.q + head;
+  const T* __restrict__ kh = (const T*)p.k + head;
+  const T* __restrict__ vh = (const T*)p.v + head;
+
+  const int qrow0 = qt * BR + w * WR;  // first query row of this wave
+  // Q operands (B of S^T = K Q^T): block qb, lane holds
+  // Q[qrow0 + 32 qb + ql][16 s + 8 g .. +8]; rows past the end read row N-1.
+  i32x4 qop[QB][NS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const T* qr = qh + (size_t)min(qrow0 + 32 * qb + ql, N - 1) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qop[qb][s] = *(const i32x4*)(qr + 16 * s);
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qop[qb][s]));  // drain before the copies
+  if (p.scale_log2 < 0.f) {  // a negative scale moves into Q's sign (exact)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qop[qb][s] ^= (int)0x80008000u;
+  }
+  const float c = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
+
+  const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
+  const int nt = (kv_end + BC - 1) / BC;
+  // Last tile this wave computes (-1: the wave's rows are all past N and it
+  // only helps with the copies).
+  const int jlast = qrow0 >= N ? -1 : (CAUSAL ? min(nt - 1, (qrow0 + WR - 1) / BC) : nt - 1);
+
+  // ---- tile copies: wave w, instruction u fills slots (u NW + w) 64 + lane ----
+  // Buffer loads against a resource that spans exactly this head's K (or V):
+  // rows past N fail the hardware range check and read as zeros, and the
+  // per-tile offset is one add.
+  uint32_t ld_voff[CPT];  // byte offset of this lane's chunk within a tile
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int s = (u * NW + w) * 64 + lane, row = s / CPR, ch = s % CPR;
+    ld_voff[u] = row * RB + (ch ^ chunk_swz<D>(row)) * 16;
+  }
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const __amdgpu_buffer_rsrc_t kbuf = make_rsrc(kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t vbuf = make_rsrc(vh, head_bytes);
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+  auto issue_tile = [&](int j) {
+    const uint32_t kdst = smem_base + (j % ST) * 2 * TB + w * 1024;
+    const uint32_t t0 = (uint32_t)j * TB;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      buf_dma16(kbuf, t0 + ld_voff[u], kdst + u * NW * 1024);
+      buf_dma16(vbuf, t0 + ld_voff[u], kdst + u * NW * 1024 + TB);
+    }
+  };
+
+  // ---- LDS read geometry ----
+  // K operand (A of S^T): row kb*32 + swap_bits23(ql), logical chunk 2 s + g.
+  // V operand (A of O^T = V^T P^T), transposed read: in each 16-lane group,
+  // lane i points at row (i/4) and column 4*(i%4) of a 4 x 16 block; the
+  // hardware returns to lane i the 4 values of column i.
+  // Per-lane byte offsets inside a stage; the stage and the 16-key half are
+  // compile-time and go into the instructions' immediate offsets.
+  const int krow = swap_bits23(ql);
+  const int ky = g ^ chunk_swz<D>(krow);
+  int kaddr[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) kaddr[s] = krow * RB + (((2 * s) ^ ky) << 4);
+  const int trow = (lane & 15) >> 2;
+  int vaddr[2][ND];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = 8 * g + 4 * t + trow;
+    const int vx = (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ chunk_swz<D>(r);
+#pragma unroll
+    for (int b = 0; b < ND; ++b) vaddr[t][b] = r * RB + 8 * (lane & 1) + (((4 * b) ^ vx) << 4);
+  }
+
+  f32x16 oacc[QB][ND];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][b][r] = 0.f;
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = kMInit;
+    l[qb] = 0.f;
+  }
+
+  typedef f32x16 STile[QB][NKB];
+  typedef i32x4 PTile[QB][NKB][2];
+
+  // S^T = K_j Q^T for both query blocks; each K operand read feeds two MFMAs
+  // (the first k-step starts from a zero accumulator).  SG = stage of tile j.
+  auto qk = [&](auto SG, STile& S) {
+    const char* sk = smem + decltype(SG)::value * 2 * TB;
+    const f32x16 zero = {};
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const i32x4 kop = *(const i32x4*)(sk + kb * 32 * RB + kaddr[s]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          S[qb][kb] = Half<T>::mfma(kop, qop[qb][s], s == 0 ? zero : S[qb][kb]);
+      }
+  };
+
+  // Hidden keys of tile j become -inf (tiles crossing the diagonal or N).
+  auto mask = [&](int j, STile& S) {
+    const int key0 = j * BC;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int lim = CAUSAL ? min(qrow0 + 32 * qb + ql, N - 1) : N - 1;
+      const int rel = lim - key0 - 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          S[qb][kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) <= rel) ? S[qb][kb][r] : kNegInf;
+    }
+  };
+  auto needs_mask = [&](int j) {
+    return (j * BC + BC > N) || (CAUSAL && j * BC + BC - 1 > qrow0);
+  };
+
+  // Online softmax of S (branch-free): running max with lazy moves, P packed
+  // to 16-bit for the second product, alpha = factor O must be scaled by.
+  auto softmax = [&](STile& S, PTile& P, float (&alpha)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], S[qb][kb][r]);
+      const float mx = pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
+      const float mt = (mx == kNegInf) ? kNegInf : mx * c;
+      const float mnew = (mt > m[qb] + kLazy) ? mt : m[qb];
+      alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mnew);
+      m[qb] = mnew;
+      const float negm = -mnew;
+      float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][kb][r], c, negm));
+          S[qb][kb][r] = pr;
+          rs4[r & 3] += pr;
+        }
+      l[qb] = l[qb] * alpha[qb] + ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            P[qb][kb][h][e] =
+                (int)Half<T>::pack2(S[qb][kb][8 * h + 2 * e], S[qb][kb][8 * h + 2 * e + 1]);
+    }
+  };
+
+  auto rescale = [&](const float (&alpha)[QB]) {
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int b = 0; b < ND; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][b][r] *= alpha[qb];
+    }
+  };
+
+  // O^T += V_j^T P^T; each V operand read feeds both query blocks.
+  auto pv = [&](auto SG, const PTile& P) {
+    const char* sv = smem + decltype(SG)::value * 2 * TB + TB;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const char* vb = sv + (kb * 32 + 16 * h) * RB;
+        i16x4 vlo[ND], vhi[ND];
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+          vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[0][b]));
+          vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[1][b]));
+        }
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+          const i16x8 v8 = {vlo[b][0], vlo[b][1], vlo[b][2], vlo[b][3],
+                            vhi[b][0], vhi[b][1], vhi[b][2], vhi[b][3]};
+          const i32x4 va = __builtin_bit_cast(i32x4, v8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][b] = Half<T>::mfma(va, P[qb][kb][h], oacc[qb][b]);
+        }
+      }
+  };
+
+  // ---- main loop: ring of ST stages, tile t copied during iteration t - 3 ----
+  // Tile j + 3 goes into the stage of tile j - 1, which every wave finished
+  // before the barrier that ended iteration j - 1.  Copies complete in order,
+  // so "tile j + 1 has landed" is vmcnt <= 2 CPT (tiles issued after it).
+  for (int t = 0; t < 3 && t < nt; ++t) issue_tile(t);
+  wait_vmcnt(2 * CPT * (min(nt, 3) - 1));
+  __syncthreads();
+
+  STile sacc;
+  PTile pt;
+  float alpha[QB];
+  // One iteration; SG = j % ST as a compile-time constant (the loop below is
+  // unrolled over the ring) so that every LDS address is register + immediate.
+  auto step = [&](int j, auto SG) {
+    if (j + 3 < nt) issue_tile(j + 3);
+    if (j <= jlast) {
+      qk(SG, sacc);
+      if (needs_mask(j)) mask(j, sacc);
+      softmax(sacc, pt, alpha);
+      rescale(alpha);
+      pv(SG, pt);
+    }
+    if (j + 3 < nt) {  // steady state: tiles j + 2 and j + 3 may stay in flight
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * CPT) : "memory");
+    } else {
+      wait_vmcnt(2 * CPT * max(0, nt - 1 - (j + 1)));
+    }
+    __syncthreads();
+  };
+  static_assert(ST == 4, "the loop below is unrolled over four ring stages");
+  for (int j = 0; j < nt; j += ST) {
+    step(j, std::integral_constant<int, 0>());
+    if (j + 1 < nt) step(j + 1, std::integral_constant<int, 1>());
+    if (j + 2 < nt) step(j + 2, std::integral_constant<int, 2>());
+    if (j + 3 < nt) step(j + 3, std::integral_constant<int, 3>());
+  }
+
+  // ---- epilogue: O = O^T / l, LSE = ln2 (m + log2 l) ----
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int myq = qrow0 + 32 * qb + ql;
+    const float lt = pair_sum(l[qb]);
+    if (myq < N) {
+      const float inv = 1.0f / lt;
+      T* orow = (T*)p.o + head + (size_t)myq * D;
+#pragma unroll
+      for (int b = 0; b < ND; ++b)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          uint2 stv;
+          stv.x = Half<T>::pack2(oacc[qb][b][4 * a] * inv, oacc[qb][b][4 * a + 1] * inv);
+          stv.y = Half<T>::pack2(oacc[qb][b][4 * a + 2] * inv, oacc[qb][b][4 * a + 3] * inv);
+          *(uint2*)(orow + 32 * b + 8 * a + 4 * g) = stv;
+        }
+      if (g == 0)
+        p.lse[(size_t)bh * N + myq] = (m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+    }
+  }
+}
+
+template <typename T, bool CAUSAL>
+hipError_t launch_wide(const FwdParams& p, hipStream_t stream) {
+  FwdParams q = p;
+  q.nq = (p.N + 255) / 256;
+  const unsigned grid = (unsigned)(q.nq * p.BH);
+  hipLaunchKernelGGL((fwd_wide<T, CAUSAL>), dim3(grid), dim3(256), 0, stream, q);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_wide(const FwdParams& p, int causal, int is_bf16, hipStream_t s) {
+  if (is_bf16) return causal ? launch_wide<__bf16, true>(p, s) : launch_wide<__bf16, false>(p, s);
+  return causal ? launch_wide<_Float16, true>(p, s) : launch_wide<_Float16, false>(p, s);
+}
+
+
+}  // namespace fa

@@ -51,6 +51,8 @@ struct QuantParams {
 
 // fp16 / bf16 inputs, MFMA path.  d in {64, 128, 256}.
 hipError_t launch_fwd_half(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
+// fp16 / bf16, d = 128: 64 query rows per wave (fa_fwd_wide.hip).
+hipError_t launch_fwd_wide(const FwdParams& p, int causal, int is_bf16, hipStream_t s);
 // fp32 inputs (v_mfma_f32_32x32x2f32).  d in {64, 128, 256}.
 hipError_t launch_fwd_f32(const FwdParams& p, int d, int causal, hipStream_t s);
 // e4m3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4).  d = 128.

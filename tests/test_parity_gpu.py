@@ -59,6 +59,23 @@ def test_small_shapes_every_element(dtype, d, N, causal):
         assert st["o_max_abs"] < 1e-4 and st["lse_max_abs"] < 1e-4, st
 
 
+# d = 128 has two kernels: causal launches whose grid of 256-row workgroups
+# fits in one round of two per CU go to the 8-wave kernel, all others to the
+# 64-rows-per-wave kernel.  The small shapes above take the first route for
+# causal masking; these head counts push small, ragged causal launches past
+# 512 workgroups so the second kernel is checked element by element too.
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("BH,N", [(520, 100), (260, 300), (176, 513)])
+def test_many_heads_causal_every_element(dtype, BH, N):
+    d = 128
+    _say(f"case many-heads causal dtype={dtype} BH={BH} N={N}")
+    q, k, v = inputs.random_inputs(1, BH, N, d, dtype, seed=BH + N)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = run_gpu(q, k, v, 1, scale)
+    o_ref, lse_ref = oracle.attention(widen(q), widen(k), widen(v), 1, scale)
+    check(o, lse, o_ref, lse_ref, dtype, f"{dtype} BH={BH} N={N} causal")
+
+
 def _sample_rows(B, H, N, seed, per_head=24, heads=6):
     rng = np.random.default_rng(seed)
     hs = sorted(set([0, B * H - 1] + list(rng.integers(0, B * H, heads - 2))))
