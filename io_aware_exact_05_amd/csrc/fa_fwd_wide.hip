@@ -128,11 +128,11 @@ void fwd_wide(FwdParams p) {
   // hardware returns to lane i the 4 values of column i.
   // Per-lane byte offsets inside a stage; the stage and the 16-key half are
   // compile-time and go into the instructions' immediate offsets.
+  // K chunk 2 s + g of row krow sits at chunk (2 s + g) ^ swz(krow); the
+  // XOR with 2 s only touches byte-offset bits 5..7, so one base register
+  // serves every k-step: address = kbase ^ (s << 5).
   const int krow = swap_bits23(ql);
-  const int ky = g ^ chunk_swz<D>(krow);
-  int kaddr[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) kaddr[s] = krow * RB + (((2 * s) ^ ky) << 4);
+  const int kbase = krow * RB + ((g ^ chunk_swz<D>(krow)) << 4);
   const int trow = (lane & 15) >> 2;
   int vaddr[2][ND];
 #pragma unroll
@@ -169,7 +169,7 @@ void fwd_wide(FwdParams p) {
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const i32x4 kop = *(const i32x4*)(sk + kb * 32 * RB + kaddr[s]);
+        const i32x4 kop = *(const i32x4*)(sk + kb * 32 * RB + (kbase ^ (s << 5)));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           S[qb][kb] = Half<T>::mfma(kop, qop[qb][s], s == 0 ? zero : S[qb][kb]);
