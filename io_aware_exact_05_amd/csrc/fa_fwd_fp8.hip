@@ -6,8 +6,8 @@
 // per-128-row fp32 descales for Q, K and V.
 //
 // Same tiling and online softmax as the 16-bit kernel: one workgroup owns
-// 128 query rows (four waves of 32), K/V tiles of 128 rows (one descale
-// block each) stream through a two-stage LDS ring filled by direct
+// 128 query rows (four waves of 32, one descale block), K/V tiles of 128
+// rows (one descale block each) stream through an LDS ring filled by direct
 // global -> LDS copies; S^T = K8 Q8^T keeps one query per lane.
 //   scores    t = s8 * (scale log2 e * q_descale[query block] *
 //             k_descale[tile]): one per-tile multiplier folded into the FMA.
@@ -69,10 +69,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Key-tile rows (64 or 128), ring stages and waves per SIMD (tuning builds
+// may override them).  Measured: 128-key tiles in a 2-stage ring at two waves
+// per SIMD beat 64-key tiles at two waves (about 12%) and at three (spills).
+#ifndef FA_FP8_BC
+#define FA_FP8_BC 128
+#endif
+#ifndef FA_FP8_ST
+#define FA_FP8_ST 2
+#endif
+#ifndef FA_FP8_OCC
+#define FA_FP8_OCC 2
+#endif
+
 template <bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FP8_OCC, FA_FP8_OCC)))
 void fwd_fp8(Fp8Params p) {
-  constexpr int D = 128, BC = 128, NW = 4, BR = 32 * NW, ST = 2;
+  constexpr int D = 128, BC = FA_FP8_BC, NW = 4, BR = 32 * NW, ST = FA_FP8_ST, PD = ST - 1;
   constexpr int RB = D;                      // bytes per fp8 row
   constexpr int TB = BC * RB;                // bytes per K or V tile
   constexpr int SB = 2 * TB;                 // ring stage: K tile, then V tile
@@ -82,7 +95,9 @@ void fwd_fp8(Fp8Params p) {
   constexpr int NKB = BC / 32;               // 32-key blocks per tile
   constexpr int NKS = BC / 64;               // MFMA k-steps of V^T P^T
   constexpr int ND = D / 32;                 // 32-column blocks of O
-  static_assert(BC == 128 && BR == 128, "tiles coincide with the 128-row descale blocks");
+  static_assert((BC == 64 || BC == 128) && BR == 128,
+                "query tiles are one 128-row descale block, key tiles a half or whole one");
+  static_assert(PD >= 1 && 2 * CPT * (PD - 1) <= 31, "ring depth");
   __shared__ __attribute__((aligned(1024))) char smem[ST * SB];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -133,8 +148,8 @@ void fwd_fp8(Fp8Params p) {
     ld_off[u] = (ch16 ^ swz8(row)) * 16;
   }
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
-  auto issue_tile = [&](int j, int stage) {
-    const uint32_t dst = smem_base + stage * SB + w * 1024;
+  auto issue_tile = [&](int j) {
+    const uint32_t dst = smem_base + (j % ST) * SB + w * 1024;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const size_t row = (size_t)min(j * BC + ld_row[u], N - 1);
@@ -161,13 +176,17 @@ void fwd_fp8(Fp8Params p) {
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float m = kMInit, l = 0.f;
 
-  issue_tile(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Ring of ST stages: tile t is copied during iteration t - PD into the stage
+  // of tile t - ST, which every wave finished before the barrier that ended
+  // iteration t - PD - 1.  Copies complete in order: "tile j + 1 has landed"
+  // is vmcnt <= 2 CPT x (tiles issued after it).
+  for (int t = 0; t < PD && t < nt; ++t) issue_tile(t);
+  wait_vmcnt(2 * CPT * (min(nt, PD) - 1));
   __syncthreads();
 
   for (int j = 0; j < nt; ++j) {
-    const int st = j & 1;
-    if (j + 1 < nt) issue_tile(j + 1, st ^ 1);
+    const int st = j % ST;
+    if (j + PD < nt) issue_tile(j + PD);
     if (j <= jlast) {
       const char* sk = smem + st * SB;
       const char* sv = sk + TB;
@@ -190,7 +209,8 @@ void fwd_fp8(Fp8Params p) {
       __builtin_amdgcn_s_setprio(0);
       // ---- scale, mask, online softmax ----
       const int key0 = j * BC;
-      const float ct = cq * kd[j];  // tile j is descale block j
+      const int blk = (j * BC) >> 7;  // the 128-row descale block of tile j
+      const float ct = cq * kd[blk];
       if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qrow0)) {
         const int lim = CAUSAL ? min(myq, N - 1) : N - 1;
         const int rel = lim - key0 - 8 * g;
@@ -220,7 +240,7 @@ void fwd_fp8(Fp8Params p) {
       }
       // v_descale = 2^e f, f in (1/2, 1]; the E8M0 scale 127 + e is kept in
       // [0, 254] (255 encodes NaN)
-      const float vdj = vd[j];
+      const float vdj = vd[blk];
       int ex = __builtin_amdgcn_frexp_expf(vdj);
       const float mant = __builtin_amdgcn_frexp_mantf(vdj);  // [1/2, 1)
       const float f = (mant == 0.5f) ? 1.0f : mant;
@@ -273,7 +293,11 @@ void fwd_fp8(Fp8Params p) {
       }
       __builtin_amdgcn_s_setprio(0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (j + PD < nt) {  // steady state: tiles j + 2 .. j + PD may stay in flight
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPT * (PD - 1)) : "memory");
+    } else {
+      wait_vmcnt(2 * CPT * max(0, nt - 1 - (j + 1)));
+    }
     __syncthreads();
   }
 
