@@ -76,7 +76,8 @@ def kernel_name(w) -> str:
         return "fwd_fp8"
     if w.dtype == "f32":
         return "fwd_f32"
-    if w.d == 128 and (not w.causal or (w.N + 255) // 256 * w.B * w.H > 512):
+    rows = {128: 256, 256: 128}.get(w.d)
+    if rows and (not w.causal or (w.N + rows - 1) // rows * w.B * w.H > 512):
         return "fwd_wide"
     return "fwd_mfma16"
 

@@ -64,8 +64,16 @@ namespace fa {
 #ifndef FA_D256_OCC
 #define FA_D256_OCC 1
 #endif
+// Which head dimensions run fwd_wide (fa_fwd_wide.hip) instead of the kernel
+// below (see use_wide for the causal case).
+#ifndef FA_D64_WIDE
+#define FA_D64_WIDE 0
+#endif
 #ifndef FA_D128_WIDE
-#define FA_D128_WIDE 1  // d = 128 runs fwd_wide (fa_fwd_wide.hip); 0 = the kernel below
+#define FA_D128_WIDE 1
+#endif
+#ifndef FA_D256_WIDE
+#define FA_D256_WIDE 1
 #endif
 #ifndef FA_D64_NW
 #define FA_D64_NW 4
@@ -402,28 +410,29 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Causal work per query tile grows with the tile index.  fwd_wide runs two
-// 256-row workgroups per CU; when its whole grid fits in one round of those
+// Causal work per query tile grows with the tile index.  fwd_wide runs a few
+// 4-wave workgroups per CU; when its whole grid fits in one round of those
 // slots the heaviest tiles alone set the runtime, and fwd_mfma16 (one 8-wave
-// workgroup per CU, two rounds, heaviest tiles first) balances better.
-static bool causal_fills_several_rounds(const FwdParams& p) {
+// workgroup per CU, more rounds, heaviest tiles first) balances better.
+static bool use_wide(const FwdParams& p, int d, int causal) {
+  const bool enabled = d == 64 ? FA_D64_WIDE : d == 128 ? FA_D128_WIDE : FA_D256_WIDE;
+  if (!enabled) return false;
+  if (!causal) return true;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  const long long grid = (long long)((p.N + 255) / 256) * p.BH;
-  return grid > 2LL * cus;
+  const int br = wide_rows_per_block(d);
+  const long long grid = (long long)((p.N + br - 1) / br) * p.BH;
+  return grid > (long long)wide_blocks_per_cu(d) * cus;
 }
 
 template <typename T>
 static hipError_t launch_t(const FwdParams& p, int d, int causal, hipStream_t s) {
+  if (use_wide(p, d, causal)) return launch_fwd_wide(p, d, causal, std::is_same<T, __bf16>::value, s);
   switch (d) {
     case 64:  return causal ? launch_one<T, 64, true>(p, s) : launch_one<T, 64, false>(p, s);
-    case 128:
-#if FA_D128_WIDE
-      if (!causal || causal_fills_several_rounds(p)) return launch_fwd_wide(p, causal, std::is_same<T, __bf16>::value, s);
-#endif
-      return causal ? launch_one<T, 128, true>(p, s) : launch_one<T, 128, false>(p, s);
+    case 128: return causal ? launch_one<T, 128, true>(p, s) : launch_one<T, 128, false>(p, s);
     case 256: return causal ? launch_one<T, 256, true>(p, s) : launch_one<T, 256, false>(p, s);
   }
   return hipErrorInvalidValue;

@@ -1,18 +1,18 @@
-// Fused exact attention forward for gfx950, fp16/bf16 inputs, d = 128.
+// Fused exact attention forward for gfx950, fp16/bf16 inputs, one wave of
+// each 4-wave workgroup per SIMD (d = 128 and d = 256).
 //
 // The method is that of "FlashAttention (HI)" (tiling, online softmax, one
 // kernel writing only O and the logsumexp); the tile shapes are chosen for
-// CDNA4.  Each wave owns 64 query rows (two 32-row MFMA blocks) and streams
+// CDNA4.  Each wave owns 32 QB query rows (QB 32-row MFMA blocks) and streams
 // 32-key tiles of K and V through LDS:
-//   * every K or V operand read from LDS feeds two MFMAs (one per query
-//     block), half the LDS traffic per flop of a 32-row wave.  With 32 rows
-//     per wave the LDS reads of a tile, plus the copies filling it, take about
-//     as long as its MFMAs, and the two units cap each other;
-//   * the whole state (O 64 x 128 fp32, the score tile, Q) fits in 256
-//     VGPRs, so two workgroups share a CU and each SIMD runs two waves: while
-//     one computes exponentials the other issues matrix products.  MFMAs are
-//     built in VGPR form (compiler flag for this file), which keeps the
-//     accumulators out of the AGPRs and avoids copies between the two files.
+//   * d = 128, QB = 2: every K or V operand read from LDS feeds two MFMAs
+//     (one per query block), half the LDS traffic per flop of a 32-row wave;
+//     the whole state (O 64 x 128 fp32, the score tile, Q) fits in 256 VGPRs,
+//     so two workgroups share a CU and each SIMD runs two waves;
+//   * d = 256, QB = 1: O 32 x 256 and Q still fit two waves per SIMD, which
+//     the 8-wave kernel cannot reach at this width.
+// MFMAs are built in VGPR form (compiler flag for this file), which keeps the
+// accumulators out of the AGPRs and avoids copies between the two files.
 // Score layout, key permutation, transposed V reads, chunk swizzle, lazy
 // running max and masking follow fwd_mfma16 (fa_fwd.hip).
 #include <hip/hip_runtime.h>
@@ -43,19 +43,54 @@ __device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
                : "memory", "m0");
 }
 
-template <typename T, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Per head dimension: QB 32-row query blocks per wave, BC keys per tile, ST
+// ring stages, OCC waves per SIMD the registers are budgeted for (one
+// 4-wave workgroup per OCC on each CU).  The FA_W* macros exist for tuning
+// builds only.
+#ifndef FA_W64_QB
+#define FA_W64_QB 2
+#endif
+#ifndef FA_W64_ST
+#define FA_W64_ST 4
+#endif
+#ifndef FA_W64_OCC
+#define FA_W64_OCC 2
+#endif
+#ifndef FA_W256_QB
+#define FA_W256_QB 1
+#endif
+#ifndef FA_W256_ST
+#define FA_W256_ST 2
+#endif
+#ifndef FA_W256_OCC
+#define FA_W256_OCC 2
+#endif
+template <int D> struct WideCfg;
+template <> struct WideCfg<64> {
+  static constexpr int QB = FA_W64_QB, BC = 32, ST = FA_W64_ST, OCC = FA_W64_OCC;
+};
+template <> struct WideCfg<128> {
+  static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2;
+};
+template <> struct WideCfg<256> {
+  static constexpr int QB = FA_W256_QB, BC = 32, ST = FA_W256_ST, OCC = FA_W256_OCC;
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WideCfg<D>::OCC, WideCfg<D>::OCC)))
 void fwd_wide(FwdParams p) {
-  constexpr int D = 128, BC = 32, NW = 4, QB = 2, WR = 32 * QB, BR = WR * NW, ST = 4;
+  constexpr int BC = WideCfg<D>::BC, NW = 4, QB = WideCfg<D>::QB, WR = 32 * QB, BR = WR * NW;
+  constexpr int ST = WideCfg<D>::ST, PD = ST - 1;
   constexpr int RB = D * 2;                  // bytes per K/V row
-  constexpr int TB = BC * RB;                // bytes per K or V tile (8 KiB)
+  constexpr int TB = BC * RB;                // bytes per K or V tile
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int CPT = BC * CPR / (64 * NW);  // copies per wave per tile and tensor
   constexpr int NS = D / 16;                 // MFMA k-steps of K Q^T
   constexpr int NKB = BC / 32;               // 32-key blocks per tile
   constexpr int ND = D / 32;                 // 32-column blocks of O
   static_assert(CPT * 64 * NW == BC * CPR, "tile must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char smem[ST * 2 * TB];  // [stage][K, V], 64 KiB
+  static_assert(PD >= 1 && 2 * CPT * (PD - 1) <= 31, "ring depth");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * 2 * TB];  // [stage][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -232,7 +267,10 @@ void fwd_wide(FwdParams p) {
   };
 
   auto rescale = [&](const float (&alpha)[QB]) {
-    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) any = any || alpha[qb] != 1.0f;
+    if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -267,12 +305,12 @@ void fwd_wide(FwdParams p) {
       }
   };
 
-  // ---- main loop: ring of ST stages, tile t copied during iteration t - 3 ----
-  // Tile j + 3 goes into the stage of tile j - 1, which every wave finished
+  // ---- main loop: ring of ST stages, tile t copied during iteration t - PD ----
+  // Tile j + PD goes into the stage of tile j - 1, which every wave finished
   // before the barrier that ended iteration j - 1.  Copies complete in order,
-  // so "tile j + 1 has landed" is vmcnt <= 2 CPT (tiles issued after it).
-  for (int t = 0; t < 3 && t < nt; ++t) issue_tile(t);
-  wait_vmcnt(2 * CPT * (min(nt, 3) - 1));
+  // so "tile j + 1 has landed" is vmcnt <= 2 CPT x (tiles issued after it).
+  for (int t = 0; t < PD && t < nt; ++t) issue_tile(t);
+  wait_vmcnt(2 * CPT * (min(nt, PD) - 1));
   __syncthreads();
 
   STile sacc;
@@ -281,7 +319,7 @@ void fwd_wide(FwdParams p) {
   // One iteration; SG = j % ST as a compile-time constant (the loop below is
   // unrolled over the ring) so that every LDS address is register + immediate.
   auto step = [&](int j, auto SG) {
-    if (j + 3 < nt) issue_tile(j + 3);
+    if (j + PD < nt) issue_tile(j + PD);
     if (j <= jlast) {
       qk(SG, sacc);
       if (needs_mask(j)) mask(j, sacc);
@@ -289,19 +327,23 @@ void fwd_wide(FwdParams p) {
       rescale(alpha);
       pv(SG, pt);
     }
-    if (j + 3 < nt) {  // steady state: tiles j + 2 and j + 3 may stay in flight
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * CPT) : "memory");
+    if (j + PD < nt) {  // steady state: tiles j + 2 .. j + PD may stay in flight
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPT * (PD - 1)) : "memory");
     } else {
       wait_vmcnt(2 * CPT * max(0, nt - 1 - (j + 1)));
     }
     __syncthreads();
   };
-  static_assert(ST == 4, "the loop below is unrolled over four ring stages");
+  static_assert(ST >= 2 && ST <= 4, "the loop below is unrolled over 2 to 4 ring stages");
   for (int j = 0; j < nt; j += ST) {
     step(j, std::integral_constant<int, 0>());
     if (j + 1 < nt) step(j + 1, std::integral_constant<int, 1>());
-    if (j + 2 < nt) step(j + 2, std::integral_constant<int, 2>());
-    if (j + 3 < nt) step(j + 3, std::integral_constant<int, 3>());
+    if constexpr (ST > 2) {
+      if (j + 2 < nt) step(j + 2, std::integral_constant<int, 2 % ST>());
+    }
+    if constexpr (ST > 3) {
+      if (j + 3 < nt) step(j + 3, std::integral_constant<int, 3 % ST>());
+    }
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 (m + log2 l) ----
@@ -327,20 +369,47 @@ void fwd_wide(FwdParams p) {
   }
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 hipError_t launch_wide(const FwdParams& p, hipStream_t stream) {
+  constexpr int BR = 32 * WideCfg<D>::QB * 4;
   FwdParams q = p;
-  q.nq = (p.N + 255) / 256;
+  q.nq = (p.N + BR - 1) / BR;
   const unsigned grid = (unsigned)(q.nq * p.BH);
-  hipLaunchKernelGGL((fwd_wide<T, CAUSAL>), dim3(grid), dim3(256), 0, stream, q);
+  hipLaunchKernelGGL((fwd_wide<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, q);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_wide_t(const FwdParams& p, int d, int causal, hipStream_t s) {
+  switch (d) {
+    case 64:  return causal ? launch_wide<T, 64, true>(p, s) : launch_wide<T, 64, false>(p, s);
+    case 128: return causal ? launch_wide<T, 128, true>(p, s) : launch_wide<T, 128, false>(p, s);
+    case 256: return causal ? launch_wide<T, 256, true>(p, s) : launch_wide<T, 256, false>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_wide(const FwdParams& p, int causal, int is_bf16, hipStream_t s) {
-  if (is_bf16) return causal ? launch_wide<__bf16, true>(p, s) : launch_wide<__bf16, false>(p, s);
-  return causal ? launch_wide<_Float16, true>(p, s) : launch_wide<_Float16, false>(p, s);
+int wide_rows_per_block(int d) {
+  switch (d) {
+    case 64: return 128 * WideCfg<64>::QB;
+    case 128: return 128 * WideCfg<128>::QB;
+    case 256: return 128 * WideCfg<256>::QB;
+  }
+  return 0;
+}
+int wide_blocks_per_cu(int d) {
+  switch (d) {
+    case 64: return WideCfg<64>::OCC;
+    case 128: return WideCfg<128>::OCC;
+    case 256: return WideCfg<256>::OCC;
+  }
+  return 0;
+}
+
+hipError_t launch_fwd_wide(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s) {
+  return is_bf16 ? launch_wide_t<__bf16>(p, d, causal, s) : launch_wide_t<_Float16>(p, d, causal, s);
 }
 
 
