@@ -422,9 +422,9 @@ static bool use_wide(const FwdParams& p, int d, int causal) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  const int br = wide_rows_per_block(d);
+  const int br = wide_rows_per_block(d, causal);
   const long long grid = (long long)((p.N + br - 1) / br) * p.BH;
-  return grid > (long long)wide_blocks_per_cu(d) * cus;
+  return grid > (long long)wide_blocks_per_cu(d, causal) * cus;
 }
 
 template <typename T>

@@ -43,44 +43,35 @@ __device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
                : "memory", "m0");
 }
 
-// Per head dimension: QB 32-row query blocks per wave, BC keys per tile, ST
-// ring stages, OCC waves per SIMD the registers are budgeted for (one
-// 4-wave workgroup per OCC on each CU).  The FA_W* macros exist for tuning
-// builds only.
-#ifndef FA_W64_QB
-#define FA_W64_QB 2
-#endif
-#ifndef FA_W64_ST
-#define FA_W64_ST 4
-#endif
-#ifndef FA_W64_OCC
-#define FA_W64_OCC 2
-#endif
-#ifndef FA_W256_QB
-#define FA_W256_QB 1
-#endif
-#ifndef FA_W256_ST
-#define FA_W256_ST 2
-#endif
-#ifndef FA_W256_OCC
-#define FA_W256_OCC 2
-#endif
-template <int D> struct WideCfg;
-template <> struct WideCfg<64> {
-  static constexpr int QB = FA_W64_QB, BC = 32, ST = FA_W64_ST, OCC = FA_W64_OCC;
-};
-template <> struct WideCfg<128> {
+// Per head dimension and masking: QB 32-row query blocks per wave, BC keys
+// per tile, ST ring stages, OCC waves per SIMD the registers are budgeted for
+// (OCC 4-wave workgroups per CU).  Measured choices:
+//   d = 128 without masking: 64 rows per wave (half the LDS reads per flop);
+//   d = 128 causal: 32 rows per wave at three waves per SIMD (twice as many
+//           workgroups, so the unequal causal tiles balance over rounds);
+//   d = 256: 32 rows per wave, two waves per SIMD.
+// d = 64 runs the 8-wave kernel (no gain measured here); its entry is kept.
+template <int D, bool CAUSAL> struct WideCfg;
+template <bool C> struct WideCfg<64, C> {
   static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2;
 };
-template <> struct WideCfg<256> {
-  static constexpr int QB = FA_W256_QB, BC = 32, ST = FA_W256_ST, OCC = FA_W256_OCC;
+template <> struct WideCfg<128, false> {
+  static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2;
+};
+template <> struct WideCfg<128, true> {
+  static constexpr int QB = 1, BC = 32, ST = 3, OCC = 3;
+};
+template <bool C> struct WideCfg<256, C> {
+  static constexpr int QB = 1, BC = 32, ST = 2, OCC = 2;
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WideCfg<D>::OCC, WideCfg<D>::OCC)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(WideCfg<D, CAUSAL>::OCC, WideCfg<D, CAUSAL>::OCC)))
 void fwd_wide(FwdParams p) {
-  constexpr int BC = WideCfg<D>::BC, NW = 4, QB = WideCfg<D>::QB, WR = 32 * QB, BR = WR * NW;
-  constexpr int ST = WideCfg<D>::ST, PD = ST - 1;
+  using Cfg = WideCfg<D, CAUSAL>;
+  constexpr int BC = Cfg::BC, NW = 4, QB = Cfg::QB, WR = 32 * QB, BR = WR * NW;
+  constexpr int ST = Cfg::ST, PD = ST - 1;
   constexpr int RB = D * 2;                  // bytes per K/V row
   constexpr int TB = BC * RB;                // bytes per K or V tile
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -371,7 +362,7 @@ void fwd_wide(FwdParams p) {
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_wide(const FwdParams& p, hipStream_t stream) {
-  constexpr int BR = 32 * WideCfg<D>::QB * 4;
+  constexpr int BR = 32 * WideCfg<D, CAUSAL>::QB * 4;
   FwdParams q = p;
   q.nq = (p.N + BR - 1) / BR;
   const unsigned grid = (unsigned)(q.nq * p.BH);
@@ -391,21 +382,29 @@ hipError_t launch_wide_t(const FwdParams& p, int d, int causal, hipStream_t s) {
 
 }  // namespace
 
-int wide_rows_per_block(int d) {
+template <bool C>
+static int rows_per_block(int d) {
   switch (d) {
-    case 64: return 128 * WideCfg<64>::QB;
-    case 128: return 128 * WideCfg<128>::QB;
-    case 256: return 128 * WideCfg<256>::QB;
+    case 64: return 128 * WideCfg<64, C>::QB;
+    case 128: return 128 * WideCfg<128, C>::QB;
+    case 256: return 128 * WideCfg<256, C>::QB;
   }
   return 0;
 }
-int wide_blocks_per_cu(int d) {
+template <bool C>
+static int blocks_per_cu(int d) {
   switch (d) {
-    case 64: return WideCfg<64>::OCC;
-    case 128: return WideCfg<128>::OCC;
-    case 256: return WideCfg<256>::OCC;
+    case 64: return WideCfg<64, C>::OCC;
+    case 128: return WideCfg<128, C>::OCC;
+    case 256: return WideCfg<256, C>::OCC;
   }
   return 0;
+}
+int wide_rows_per_block(int d, int causal) {
+  return causal ? rows_per_block<true>(d) : rows_per_block<false>(d);
+}
+int wide_blocks_per_cu(int d, int causal) {
+  return causal ? blocks_per_cu<true>(d) : blocks_per_cu<false>(d);
 }
 
 hipError_t launch_fwd_wide(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s) {

@@ -55,8 +55,8 @@ hipError_t launch_fwd_half(const FwdParams& p, int d, int causal, int is_bf16, h
 // workgroup per SIMD (fa_fwd_wide.hip).  d in {64, 128, 256}.
 hipError_t launch_fwd_wide(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
 // Query rows per workgroup and workgroups per CU of that kernel.
-int wide_rows_per_block(int d);
-int wide_blocks_per_cu(int d);
+int wide_rows_per_block(int d, int causal);
+int wide_blocks_per_cu(int d, int causal);
 // fp32 inputs (v_mfma_f32_32x32x2f32).  d in {64, 128, 256}.
 hipError_t launch_fwd_f32(const FwdParams& p, int d, int causal, hipStream_t s);
 // e4m3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4).  d = 128.

@@ -59,16 +59,17 @@ def test_small_shapes_every_element(dtype, d, N, causal):
         assert st["o_max_abs"] < 1e-4 and st["lse_max_abs"] < 1e-4, st
 
 
-# d = 128 has two kernels: causal launches whose grid of 256-row workgroups
-# fits in one round of two per CU go to the 8-wave kernel, all others to the
-# 64-rows-per-wave kernel.  The small shapes above take the first route for
+# d = 128 and d = 256 have two kernels each: causal launches whose grid fits
+# in one round of the one-wave-per-SIMD kernel's slots (three 128-row
+# workgroups per CU at d = 128, two at d = 256) go to the 8-wave kernel, all
+# others to the former.  The small shapes above take the first route for
 # causal masking; these head counts push small, ragged causal launches past
-# 512 workgroups so the second kernel is checked element by element too.
+# 768 workgroups so the second kernel is checked element by element too.
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("BH,N", [(520, 100), (260, 300), (176, 513)])
-def test_many_heads_causal_every_element(dtype, BH, N):
-    d = 128
-    _say(f"case many-heads causal dtype={dtype} BH={BH} N={N}")
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("BH,N", [(800, 100), (400, 300), (260, 257)])
+def test_many_heads_causal_every_element(dtype, d, BH, N):
+    _say(f"case many-heads causal dtype={dtype} d={d} BH={BH} N={N}")
     q, k, v = inputs.random_inputs(1, BH, N, d, dtype, seed=BH + N)
     scale = float(np.float32(1 / math.sqrt(d)))
     o, lse = run_gpu(q, k, v, 1, scale)
