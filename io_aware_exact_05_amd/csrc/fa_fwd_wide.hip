@@ -1,5 +1,5 @@
-// Fused exact attention forward for gfx950, fp16/bf16 inputs, one wave of
-// each 4-wave workgroup per SIMD (d = 128 and d = 256).
+// Fused exact attention forward for gfx950, fp16/bf16 inputs (d = 128 and
+// d = 256): few waves per SIMD, each owning 32 or 64 query rows.
 //
 // The method is that of "FlashAttention (HI)" (tiling, online softmax, one
 // kernel writing only O and the logsumexp); the tile shapes are chosen for
@@ -8,7 +8,8 @@
 //   * d = 128, QB = 2: every K or V operand read from LDS feeds two MFMAs
 //     (one per query block), half the LDS traffic per flop of a 32-row wave;
 //     the whole state (O 64 x 128 fp32, the score tile, Q) fits in 256 VGPRs,
-//     so two workgroups share a CU and each SIMD runs two waves;
+//     so each SIMD runs two waves, one from each half of an 8-wave workgroup,
+//     offset by half a tile so one's softmax overlaps the other's MFMAs;
 //   * d = 256, QB = 1: O 32 x 256 and Q still fit two waves per SIMD, which
 //     the 8-wave kernel cannot reach at this width.
 // MFMAs are built in VGPR form (compiler flag for this file), which keeps the
@@ -44,9 +45,12 @@ __device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 }
 
 // Per head dimension and masking: QB 32-row query blocks per wave, BC keys
-// per tile, ST ring stages, OCC waves per SIMD the registers are budgeted for
-// (OCC 4-wave workgroups per CU).  Measured choices:
-//   d = 128 without masking: 64 rows per wave (half the LDS reads per flop);
+// per tile, ST ring stages, OCC waves per SIMD the registers are budgeted for,
+// NW waves per workgroup (4 when not named).  Measured choices:
+//   d = 128 without masking: 64 rows per wave (half the LDS reads per flop),
+//           one 8-wave workgroup per CU whose two halves run half a tile
+//           apart (the lagging half keeps its packed P across the barrier;
+//           3.5-5% over two uncoordinated 4-wave workgroups);
 //   d = 128 causal: 32 rows per wave at three waves per SIMD (twice as many
 //           workgroups, so the unequal causal tiles balance over rounds);
 //   d = 256: 32 rows per wave, two waves per SIMD.
@@ -56,7 +60,7 @@ template <bool C> struct WideCfg<64, C> {
   static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2;
 };
 template <> struct WideCfg<128, false> {
-  static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2;
+  static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2, NW = 8;
 };
 template <> struct WideCfg<128, true> {
   static constexpr int QB = 1, BC = 32, ST = 3, OCC = 3;
@@ -65,13 +69,18 @@ template <bool C> struct WideCfg<256, C> {
   static constexpr int QB = 1, BC = 32, ST = 2, OCC = 2;
 };
 
+// Waves per workgroup: 4 unless the configuration names 8 (ping-pong halves).
+template <typename C, typename = void> struct NWOf { static constexpr int v = 4; };
+template <typename C> struct NWOf<C, std::void_t<decltype(C::NW)>> { static constexpr int v = C::NW; };
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__((64 * NWOf<WideCfg<D, CAUSAL>>::v))
 __attribute__((amdgpu_waves_per_eu(WideCfg<D, CAUSAL>::OCC, WideCfg<D, CAUSAL>::OCC)))
 void fwd_wide(FwdParams p) {
   using Cfg = WideCfg<D, CAUSAL>;
-  constexpr int BC = Cfg::BC, NW = 4, QB = Cfg::QB, WR = 32 * QB, BR = WR * NW;
-  constexpr int ST = Cfg::ST, PD = ST - 1;
+  constexpr int NW = NWOf<Cfg>::v;
+  constexpr bool PP = NW == 8;
+  constexpr int BC = Cfg::BC, QB = Cfg::QB, WR = 32 * QB, BR = WR * NW;
+  constexpr int ST = Cfg::ST, PD = PP ? ST - 2 : ST - 1;
   constexpr int RB = D * 2;                  // bytes per K/V row
   constexpr int TB = BC * RB;                // bytes per K or V tile
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -309,14 +318,28 @@ void fwd_wide(FwdParams p) {
   float alpha[QB];
   // One iteration; SG = j % ST as a compile-time constant (the loop below is
   // unrolled over the ring) so that every LDS address is register + immediate.
-  auto step = [&](int j, auto SG) {
+  const bool lag = PP && w >= NW / 2;
+  auto step = [&](int j, auto SG, auto LAG) __attribute__((always_inline)) {
+    constexpr int sp = (decltype(SG)::value + ST - 1) % ST;
     if (j + PD < nt) issue_tile(j + PD);
-    if (j <= jlast) {
-      qk(SG, sacc);
-      if (needs_mask(j)) mask(j, sacc);
-      softmax(sacc, pt, alpha);
-      rescale(alpha);
-      pv(SG, pt);
+    if constexpr (!decltype(LAG)::value) {
+      if (j <= jlast) {
+        qk(SG, sacc);
+        if (needs_mask(j)) mask(j, sacc);
+        softmax(sacc, pt, alpha);
+        rescale(alpha);
+        pv(SG, pt);
+      }
+    } else {
+      // the lagging half: P V of the previous tile, then scores and softmax of
+      // this one; its packed P waits across the barrier
+      if (j >= 1 && j - 1 <= jlast) pv(std::integral_constant<int, sp>(), pt);
+      if (j <= jlast) {
+        qk(SG, sacc);
+        if (needs_mask(j)) mask(j, sacc);
+        softmax(sacc, pt, alpha);
+        rescale(alpha);
+      }
     }
     if (j + PD < nt) {  // steady state: tiles j + 2 .. j + PD may stay in flight
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPT * (PD - 1)) : "memory");
@@ -325,15 +348,31 @@ void fwd_wide(FwdParams p) {
     }
     __syncthreads();
   };
-  static_assert(ST >= 2 && ST <= 4, "the loop below is unrolled over 2 to 4 ring stages");
-  for (int j = 0; j < nt; j += ST) {
-    step(j, std::integral_constant<int, 0>());
-    if (j + 1 < nt) step(j + 1, std::integral_constant<int, 1>());
-    if constexpr (ST > 2) {
-      if (j + 2 < nt) step(j + 2, std::integral_constant<int, 2 % ST>());
+  static_assert(ST >= 2 && ST <= 6, "the loop below is unrolled over 2 to 6 ring stages");
+  auto run = [&](auto LAG) __attribute__((always_inline)) {
+    for (int j = 0; j < nt; j += ST) {
+      step(j, std::integral_constant<int, 0>(), LAG);
+      if (j + 1 < nt) step(j + 1, std::integral_constant<int, 1>(), LAG);
+      if constexpr (ST > 2) { if (j + 2 < nt) step(j + 2, std::integral_constant<int, 2 % ST>(), LAG); }
+      if constexpr (ST > 3) { if (j + 3 < nt) step(j + 3, std::integral_constant<int, 3 % ST>(), LAG); }
+      if constexpr (ST > 4) { if (j + 4 < nt) step(j + 4, std::integral_constant<int, 4 % ST>(), LAG); }
+      if constexpr (ST > 5) { if (j + 5 < nt) step(j + 5, std::integral_constant<int, 5 % ST>(), LAG); }
     }
-    if constexpr (ST > 3) {
-      if (j + 3 < nt) step(j + 3, std::integral_constant<int, 3 % ST>());
+  };
+  if constexpr (PP) {
+    if (lag) run(std::true_type());
+    else run(std::false_type());
+  } else {
+    run(std::false_type());
+  }
+  if (lag && nt - 1 <= jlast) {  // the lagging half's last P V
+    switch ((nt - 1) % ST) {
+      case 0: pv(std::integral_constant<int, 0>(), pt); break;
+      case 1: pv(std::integral_constant<int, 1 % ST>(), pt); break;
+      case 2: pv(std::integral_constant<int, 2 % ST>(), pt); break;
+      case 3: pv(std::integral_constant<int, 3 % ST>(), pt); break;
+      case 4: pv(std::integral_constant<int, 4 % ST>(), pt); break;
+      default: pv(std::integral_constant<int, 5 % ST>(), pt); break;
     }
   }
 
@@ -362,11 +401,12 @@ void fwd_wide(FwdParams p) {
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_wide(const FwdParams& p, hipStream_t stream) {
-  constexpr int BR = 32 * WideCfg<D, CAUSAL>::QB * 4;
+  constexpr int NW = NWOf<WideCfg<D, CAUSAL>>::v;
+  constexpr int BR = 32 * WideCfg<D, CAUSAL>::QB * NW;
   FwdParams q = p;
   q.nq = (p.N + BR - 1) / BR;
   const unsigned grid = (unsigned)(q.nq * p.BH);
-  hipLaunchKernelGGL((fwd_wide<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, q);
+  hipLaunchKernelGGL((fwd_wide<T, D, CAUSAL>), dim3(grid), dim3(64 * NW), 0, stream, q);
   return hipGetLastError();
 }
 
@@ -386,7 +426,7 @@ template <bool C>
 static int rows_per_block(int d) {
   switch (d) {
     case 64: return 128 * WideCfg<64, C>::QB;
-    case 128: return 128 * WideCfg<128, C>::QB;
+    case 128: return 32 * NWOf<WideCfg<128, C>>::v * WideCfg<128, C>::QB;
     case 256: return 128 * WideCfg<256, C>::QB;
   }
   return 0;
