@@ -124,7 +124,7 @@ template <> struct Half<_Float16> {
 // row%16 onto 0..7 that, paired with the row's half of the line, is again a
 // bijection, and differs in bit 2 between rows r and r+2.
 template <int D>
-__device__ __forceinline__ int chunk_swz(int row) {
+__host__ __device__ constexpr int chunk_swz(int row) {
   if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   else return ((row & 3) << 2) | ((row >> 2) & 3);
 }

@@ -29,8 +29,14 @@ namespace {
 
 // Raw buffer resource over [base, base + bytes) (stride 0; data format 32 bit,
 // the value the gfx9 family expects for untyped buffer loads).
+// The base address and size go through readfirstlane: the resource must
+// live in scalar registers, and this states that they are wave-uniform.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // 16-byte buffer -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane i's
@@ -44,9 +50,21 @@ __device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
                : "memory", "m0");
 }
 
+// True when, for every row r of a transposed V read (r = 8 g + i, i < 4), the
+// swizzle of row r + 4 is that of row r with bit 0 flipped.
+template <int D>
+constexpr bool swz_step4_is_xor1() {
+  for (int g = 0; g < 2; ++g)
+    for (int i = 0; i < 4; ++i)
+      if (chunk_swz<D>(8 * g + i + 4) != (chunk_swz<D>(8 * g + i) ^ 1)) return false;
+  return true;
+}
+
 // Per head dimension and masking: QB 32-row query blocks per wave, BC keys
 // per tile, ST ring stages, OCC waves per SIMD the registers are budgeted for,
-// NW waves per workgroup (4 when not named).  Measured choices:
+// NW waves per workgroup (4 when not named); XK / XV: K / V LDS addresses
+// formed inside the loop from one base register (XORs per tile) rather than
+// kept as eight loop-invariant registers each.  Measured choices:
 //   d = 128 without masking: 64 rows per wave (half the LDS reads per flop),
 //           one 8-wave workgroup per CU whose two halves run half a tile
 //           apart (the lagging half keeps its packed P across the barrier;
@@ -58,20 +76,27 @@ __device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 template <int D, bool CAUSAL> struct WideCfg;
 template <bool C> struct WideCfg<64, C> {
   static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2;
+  static constexpr bool XK = true, XV = true;
 };
 template <> struct WideCfg<128, false> {
   static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2, NW = 8;
+  static constexpr bool XK = false, XV = false;
 };
 template <> struct WideCfg<128, true> {
   static constexpr int QB = 1, BC = 32, ST = 3, OCC = 3;
+  static constexpr bool XK = false, XV = false;
 };
 template <bool C> struct WideCfg<256, C> {
   static constexpr int QB = 1, BC = 32, ST = 2, OCC = 2;
+  static constexpr bool XK = true, XV = true;
 };
 
 // Waves per workgroup: 4 unless the configuration names 8 (ping-pong halves).
 template <typename C, typename = void> struct NWOf { static constexpr int v = 4; };
 template <typename C> struct NWOf<C, std::void_t<decltype(C::NW)>> { static constexpr int v = C::NW; };
+// K operand reads kept in flight ahead of the MFMAs (0: the compiler's order).
+template <typename C, typename = void> struct KPFOf { static constexpr int v = 0; };
+template <typename C> struct KPFOf<C, std::void_t<decltype(C::KPF)>> { static constexpr int v = C::KPF; };
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__((64 * NWOf<WideCfg<D, CAUSAL>>::v))
 __attribute__((amdgpu_waves_per_eu(WideCfg<D, CAUSAL>::OCC, WideCfg<D, CAUSAL>::OCC)))
@@ -107,23 +132,8 @@ void fwd_wide(FwdParams p) {
   const int qrow0 = qt * BR + w * WR;  // first query row of this wave
   // Q operands (B of S^T = K Q^T): block qb, lane holds
   // Q[qrow0 + 32 qb + ql][16 s + 8 g .. +8]; rows past the end read row N-1.
+  // Loaded after the first tile copies are issued (below).
   i32x4 qop[QB][NS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const T* qr = qh + (size_t)min(qrow0 + 32 * qb + ql, N - 1) * D + 8 * g;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qop[qb][s] = *(const i32x4*)(qr + 16 * s);
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qop[qb][s]));  // drain before the copies
-  if (p.scale_log2 < 0.f) {  // a negative scale moves into Q's sign (exact)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) qop[qb][s] ^= (int)0x80008000u;
-  }
   const float c = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
 
   const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
@@ -168,15 +178,16 @@ void fwd_wide(FwdParams p) {
   // serves every k-step: address = kbase ^ (s << 5).
   const int krow = swap_bits23(ql);
   const int kbase = krow * RB + ((g ^ chunk_swz<D>(krow)) << 4);
+  // One base register serves all of them.  Rows r + 4 t (t = 0, 1): r has
+  // bit 2 clear, and adding 4 to r flips bit 0 of its swizzle, so the second
+  // group sits at vaddr ^ (4 RB + 16).  Column block b sits at ^ (b << 6):
+  // the chunk index 4 b + c' is XORed with the swizzle, which only touches
+  // offset bits 4..7 (4..8 at d = 256), below the row's bits.
   const int trow = (lane & 15) >> 2;
-  int vaddr[2][ND];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int r = 8 * g + 4 * t + trow;
-    const int vx = (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ chunk_swz<D>(r);
-#pragma unroll
-    for (int b = 0; b < ND; ++b) vaddr[t][b] = r * RB + 8 * (lane & 1) + (((4 * b) ^ vx) << 4);
-  }
+  const int vrow = 8 * g + trow;
+  const int vaddr = vrow * RB + 8 * (lane & 1) +
+                    (((2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ chunk_swz<D>(vrow)) << 4);
+  static_assert(swz_step4_is_xor1<D>(), "rows r and r + 4 differ in bit 0 of the swizzle");
 
   f32x16 oacc[QB][ND];
 #pragma unroll
@@ -200,15 +211,35 @@ void fwd_wide(FwdParams p) {
   auto qk = [&](auto SG, STile& S) {
     const char* sk = smem + decltype(SG)::value * 2 * TB;
     const f32x16 zero = {};
+    // With XK the per-step addresses are formed here, not hoisted out of the
+    // loop as eight loop-invariant registers: the empty asm makes the base opaque.
+    int kb0 = kbase;
+    if constexpr (Cfg::XK) asm volatile("" : "+v"(kb0));
+    constexpr int NM = NKB * NS;
+    i32x4 kop[NM];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int i = 0; i < NM; ++i) {
+      const int kb = i % NKB, s = i / NKB;
+      kop[i] = *(const i32x4*)(sk + kb * 32 * RB + (kb0 ^ (s << 5)));
+    }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const i32x4 kop = *(const i32x4*)(sk + kb * 32 * RB + (kbase ^ (s << 5)));
+    for (int i = 0; i < NM; ++i) {
+      const int kb = i % NKB, s = i / NKB;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          S[qb][kb] = Half<T>::mfma(kop, qop[qb][s], s == 0 ? zero : S[qb][kb]);
+      for (int qb = 0; qb < QB; ++qb)
+        S[qb][kb] = Half<T>::mfma(kop[i], qop[qb][s], s == 0 ? zero : S[qb][kb]);
+    }
+    // KPF > 0: K operands are read KPF steps ahead of their MFMAs, so that
+    // the LDS latency hides behind the MFMA chain.
+    if constexpr (KPFOf<Cfg>::v > 0) {
+      constexpr int KPF = KPFOf<Cfg>::v;
+      __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        if (i + KPF < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+    }
   };
 
   // Hidden keys of tile j become -inf (tiles crossing the diagonal or N).
@@ -234,25 +265,27 @@ void fwd_wide(FwdParams p) {
   auto softmax = [&](STile& S, PTile& P, float (&alpha)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+      // four independent chains, started from the first four scores
+      float mx4[4] = {S[qb][0][0], S[qb][0][1], S[qb][0][2], S[qb][0][3]};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], S[qb][kb][r]);
+        for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], S[qb][kb][r]);
       const float mx = pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
       const float mt = (mx == kNegInf) ? kNegInf : mx * c;
       const float mnew = (mt > m[qb] + kLazy) ? mt : m[qb];
       alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mnew);
       m[qb] = mnew;
       const float negm = -mnew;
-      float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+      float rs4[4];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][kb][r], c, negm));
           S[qb][kb][r] = pr;
-          rs4[r & 3] += pr;
+          if (kb == 0 && r < 4) rs4[r] = pr;
+          else rs4[r & 3] += pr;
         }
       l[qb] = l[qb] * alpha[qb] + ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));
 #pragma unroll
@@ -283,6 +316,9 @@ void fwd_wide(FwdParams p) {
   // O^T += V_j^T P^T; each V operand read feeds both query blocks.
   auto pv = [&](auto SG, const PTile& P) {
     const char* sv = smem + decltype(SG)::value * 2 * TB + TB;
+    int va0 = vaddr;
+    if constexpr (Cfg::XV) asm volatile("" : "+v"(va0));  // as in qk
+    const int va[2] = {va0, va0 ^ (4 * RB + 16)};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -291,8 +327,8 @@ void fwd_wide(FwdParams p) {
         i16x4 vlo[ND], vhi[ND];
 #pragma unroll
         for (int b = 0; b < ND; ++b) {
-          vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[0][b]));
-          vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[1][b]));
+          vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + (va[0] ^ (b << 6))));
+          vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + (va[1] ^ (b << 6))));
         }
 #pragma unroll
         for (int b = 0; b < ND; ++b) {
@@ -309,8 +345,27 @@ void fwd_wide(FwdParams p) {
   // Tile j + PD goes into the stage of tile j - 1, which every wave finished
   // before the barrier that ended iteration j - 1.  Copies complete in order,
   // so "tile j + 1 has landed" is vmcnt <= 2 CPT x (tiles issued after it).
+  // The first tiles are issued before Q is read, so that both latencies
+  // overlap; Q's loads are the newest, and draining them drains the copies.
   for (int t = 0; t < PD && t < nt; ++t) issue_tile(t);
-  wait_vmcnt(2 * CPT * (min(nt, PD) - 1));
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const T* qr = qh + (size_t)min(qrow0 + 32 * qb + ql, N - 1) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qop[qb][s] = *(const i32x4*)(qr + 16 * s);
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qop[qb][s]));  // drain: Q and the first tiles
+  if (p.scale_log2 < 0.f) {  // a negative scale moves into Q's sign (exact)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qop[qb][s] ^= (int)0x80008000u;
+  }
+
+  wait_vmcnt(0);
   __syncthreads();
 
   STile sacc;
@@ -349,14 +404,17 @@ void fwd_wide(FwdParams p) {
     __syncthreads();
   };
   static_assert(ST >= 2 && ST <= 6, "the loop below is unrolled over 2 to 6 ring stages");
+  // With ping-pong halves both run one extra iteration (j = nt): the lagging
+  // half does its last P V there, the leading half only meets the barrier.
+  const int nsteps = PP ? nt + 1 : nt;
   auto run = [&](auto LAG) __attribute__((always_inline)) {
-    for (int j = 0; j < nt; j += ST) {
+    for (int j = 0; j < nsteps; j += ST) {
       step(j, std::integral_constant<int, 0>(), LAG);
-      if (j + 1 < nt) step(j + 1, std::integral_constant<int, 1>(), LAG);
-      if constexpr (ST > 2) { if (j + 2 < nt) step(j + 2, std::integral_constant<int, 2 % ST>(), LAG); }
-      if constexpr (ST > 3) { if (j + 3 < nt) step(j + 3, std::integral_constant<int, 3 % ST>(), LAG); }
-      if constexpr (ST > 4) { if (j + 4 < nt) step(j + 4, std::integral_constant<int, 4 % ST>(), LAG); }
-      if constexpr (ST > 5) { if (j + 5 < nt) step(j + 5, std::integral_constant<int, 5 % ST>(), LAG); }
+      if (j + 1 < nsteps) step(j + 1, std::integral_constant<int, 1>(), LAG);
+      if constexpr (ST > 2) { if (j + 2 < nsteps) step(j + 2, std::integral_constant<int, 2 % ST>(), LAG); }
+      if constexpr (ST > 3) { if (j + 3 < nsteps) step(j + 3, std::integral_constant<int, 3 % ST>(), LAG); }
+      if constexpr (ST > 4) { if (j + 4 < nsteps) step(j + 4, std::integral_constant<int, 4 % ST>(), LAG); }
+      if constexpr (ST > 5) { if (j + 5 < nsteps) step(j + 5, std::integral_constant<int, 5 % ST>(), LAG); }
     }
   };
   if constexpr (PP) {
@@ -365,37 +423,40 @@ void fwd_wide(FwdParams p) {
   } else {
     run(std::false_type());
   }
-  if (lag && nt - 1 <= jlast) {  // the lagging half's last P V
-    switch ((nt - 1) % ST) {
-      case 0: pv(std::integral_constant<int, 0>(), pt); break;
-      case 1: pv(std::integral_constant<int, 1 % ST>(), pt); break;
-      case 2: pv(std::integral_constant<int, 2 % ST>(), pt); break;
-      case 3: pv(std::integral_constant<int, 3 % ST>(), pt); break;
-      case 4: pv(std::integral_constant<int, 4 % ST>(), pt); break;
-      default: pv(std::integral_constant<int, 5 % ST>(), pt); break;
-    }
-  }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 (m + log2 l) ----
+  // A lane holds one query's O row in 8-byte pieces.  Each wave stages its 32
+  // rows of a query block in LDS (the ring is idle after the last barrier),
+  // then writes whole rows: every store instruction covers 64 / CPR rows of
+  // contiguous memory.  Chunks are XOR-swizzled by row in the staging buffer.
+  static_assert(NW * 32 * RB <= ST * 2 * TB, "staging fits in the ring");
+  char* stg = smem + w * (32 * RB);
+  T* __restrict__ oh = (T*)p.o + head;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int myq = qrow0 + 32 * qb + ql;
     const float lt = pair_sum(l[qb]);
-    if (myq < N) {
-      const float inv = 1.0f / lt;
-      T* orow = (T*)p.o + head + (size_t)myq * D;
+    const float inv = 1.0f / lt;
 #pragma unroll
-      for (int b = 0; b < ND; ++b)
+    for (int b = 0; b < ND; ++b)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          uint2 stv;
-          stv.x = Half<T>::pack2(oacc[qb][b][4 * a] * inv, oacc[qb][b][4 * a + 1] * inv);
-          stv.y = Half<T>::pack2(oacc[qb][b][4 * a + 2] * inv, oacc[qb][b][4 * a + 3] * inv);
-          *(uint2*)(orow + 32 * b + 8 * a + 4 * g) = stv;
-        }
-      if (g == 0)
-        p.lse[(size_t)bh * N + myq] = (m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+      for (int a = 0; a < 4; ++a) {
+        uint2 stv;
+        stv.x = Half<T>::pack2(oacc[qb][b][4 * a] * inv, oacc[qb][b][4 * a + 1] * inv);
+        stv.y = Half<T>::pack2(oacc[qb][b][4 * a + 2] * inv, oacc[qb][b][4 * a + 3] * inv);
+        *(uint2*)(stg + ql * RB + (((4 * b + a) ^ (ql & (CPR - 1))) << 4) + 8 * g) = stv;
+      }
+    if (g == 0 && myq < N)
+      p.lse[(size_t)bh * N + myq] = (m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are staged
+#pragma unroll
+    for (int it = 0; it < 32 * CPR / 64; ++it) {
+      const int idx = it * 64 + lane, row = idx / CPR, ch = idx % CPR;
+      const i32x4 val = *(const i32x4*)(stg + row * RB + ((ch ^ (row & (CPR - 1))) << 4));
+      const int grow = qrow0 + 32 * qb + row;
+      if (grow < N) *(i32x4*)(oh + (size_t)grow * D + ch * 8) = val;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next block's writes
   }
 }
 
