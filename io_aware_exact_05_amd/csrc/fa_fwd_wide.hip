@@ -94,9 +94,6 @@ template <bool C> struct WideCfg<256, C> {
 // Waves per workgroup: 4 unless the configuration names 8 (ping-pong halves).
 template <typename C, typename = void> struct NWOf { static constexpr int v = 4; };
 template <typename C> struct NWOf<C, std::void_t<decltype(C::NW)>> { static constexpr int v = C::NW; };
-// K operand reads kept in flight ahead of the MFMAs (0: the compiler's order).
-template <typename C, typename = void> struct KPFOf { static constexpr int v = 0; };
-template <typename C> struct KPFOf<C, std::void_t<decltype(C::KPF)>> { static constexpr int v = C::KPF; };
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__((64 * NWOf<WideCfg<D, CAUSAL>>::v))
 __attribute__((amdgpu_waves_per_eu(WideCfg<D, CAUSAL>::OCC, WideCfg<D, CAUSAL>::OCC)))
@@ -229,17 +226,6 @@ void fwd_wide(FwdParams p) {
       for (int qb = 0; qb < QB; ++qb)
         S[qb][kb] = Half<T>::mfma(kop[i], qop[qb][s], s == 0 ? zero : S[qb][kb]);
     }
-    // KPF > 0: K operands are read KPF steps ahead of their MFMAs, so that
-    // the LDS latency hides behind the MFMA chain.
-    if constexpr (KPFOf<Cfg>::v > 0) {
-      constexpr int KPF = KPFOf<Cfg>::v;
-      __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-        if (i + KPF < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
   };
 
   // Hidden keys of tile j become -inf (tiles crossing the diagonal or N).
@@ -342,9 +328,11 @@ void fwd_wide(FwdParams p) {
   };
 
   // ---- main loop: ring of ST stages, tile t copied during iteration t - PD ----
-  // Tile j + PD goes into the stage of tile j - 1, which every wave finished
-  // before the barrier that ended iteration j - 1.  Copies complete in order,
-  // so "tile j + 1 has landed" is vmcnt <= 2 CPT x (tiles issued after it).
+  // Tile j + PD goes into the stage of tile j - 1 (j - 2 with ping-pong
+  // halves, whose upper half reads tile j - 1 in iteration j), which every
+  // wave finished before the barrier that ended iteration j - 1.  Copies
+  // complete in order, so "tile j + 1 has landed" is vmcnt <= 2 CPT x (tiles
+  // issued after it).
   // The first tiles are issued before Q is read, so that both latencies
   // overlap; Q's loads are the newest, and draining them drains the copies.
   for (int t = 0; t < PD && t < nt; ++t) issue_tile(t);
@@ -371,13 +359,19 @@ void fwd_wide(FwdParams p) {
   STile sacc;
   PTile pt;
   float alpha[QB];
+  // Ping-pong halves (8-wave workgroups; waves w and w + NW/2 share a SIMD):
+  // the upper half runs mode 1 (P V of tile j - 1, then scores and softmax
+  // of tile j; its packed P waits across the barrier), the lower half mode 0
+  // (scores, softmax and P V of tile j), so the two halves' matrix products
+  // and softmaxes fall half a tile apart.
+  const bool upper = PP && w >= NW / 2;
   // One iteration; SG = j % ST as a compile-time constant (the loop below is
   // unrolled over the ring) so that every LDS address is register + immediate.
-  const bool lag = PP && w >= NW / 2;
-  auto step = [&](int j, auto SG, auto LAG) __attribute__((always_inline)) {
+  auto step = [&](int j, auto SG, auto MODE) __attribute__((always_inline)) {
     constexpr int sp = (decltype(SG)::value + ST - 1) % ST;
+    constexpr int md = decltype(MODE)::value;
     if (j + PD < nt) issue_tile(j + PD);
-    if constexpr (!decltype(LAG)::value) {
+    if constexpr (md == 0) {
       if (j <= jlast) {
         qk(SG, sacc);
         if (needs_mask(j)) mask(j, sacc);
@@ -386,8 +380,6 @@ void fwd_wide(FwdParams p) {
         pv(SG, pt);
       }
     } else {
-      // the lagging half: P V of the previous tile, then scores and softmax of
-      // this one; its packed P waits across the barrier
       if (j >= 1 && j - 1 <= jlast) pv(std::integral_constant<int, sp>(), pt);
       if (j <= jlast) {
         qk(SG, sacc);
@@ -407,21 +399,21 @@ void fwd_wide(FwdParams p) {
   // With ping-pong halves both run one extra iteration (j = nt): the lagging
   // half does its last P V there, the leading half only meets the barrier.
   const int nsteps = PP ? nt + 1 : nt;
-  auto run = [&](auto LAG) __attribute__((always_inline)) {
+  auto run = [&](auto MODE) __attribute__((always_inline)) {
     for (int j = 0; j < nsteps; j += ST) {
-      step(j, std::integral_constant<int, 0>(), LAG);
-      if (j + 1 < nsteps) step(j + 1, std::integral_constant<int, 1>(), LAG);
-      if constexpr (ST > 2) { if (j + 2 < nsteps) step(j + 2, std::integral_constant<int, 2 % ST>(), LAG); }
-      if constexpr (ST > 3) { if (j + 3 < nsteps) step(j + 3, std::integral_constant<int, 3 % ST>(), LAG); }
-      if constexpr (ST > 4) { if (j + 4 < nsteps) step(j + 4, std::integral_constant<int, 4 % ST>(), LAG); }
-      if constexpr (ST > 5) { if (j + 5 < nsteps) step(j + 5, std::integral_constant<int, 5 % ST>(), LAG); }
+      step(j, std::integral_constant<int, 0>(), MODE);
+      if (j + 1 < nsteps) step(j + 1, std::integral_constant<int, 1>(), MODE);
+      if constexpr (ST > 2) { if (j + 2 < nsteps) step(j + 2, std::integral_constant<int, 2 % ST>(), MODE); }
+      if constexpr (ST > 3) { if (j + 3 < nsteps) step(j + 3, std::integral_constant<int, 3 % ST>(), MODE); }
+      if constexpr (ST > 4) { if (j + 4 < nsteps) step(j + 4, std::integral_constant<int, 4 % ST>(), MODE); }
+      if constexpr (ST > 5) { if (j + 5 < nsteps) step(j + 5, std::integral_constant<int, 5 % ST>(), MODE); }
     }
   };
   if constexpr (PP) {
-    if (lag) run(std::true_type());
-    else run(std::false_type());
+    if (upper) run(std::integral_constant<int, 1>());
+    else run(std::integral_constant<int, 0>());
   } else {
-    run(std::false_type());
+    run(std::integral_constant<int, 0>());
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 (m + log2 l) ----
@@ -492,12 +484,17 @@ static int rows_per_block(int d) {
   }
   return 0;
 }
+// Workgroups per CU: OCC waves per SIMD, four SIMDs, NW waves per workgroup.
+template <int D, bool C>
+static constexpr int wgs_per_cu() {
+  return WideCfg<D, C>::OCC * 4 / NWOf<WideCfg<D, C>>::v;
+}
 template <bool C>
 static int blocks_per_cu(int d) {
   switch (d) {
-    case 64: return WideCfg<64, C>::OCC;
-    case 128: return WideCfg<128, C>::OCC;
-    case 256: return WideCfg<256, C>::OCC;
+    case 64: return wgs_per_cu<64, C>();
+    case 128: return wgs_per_cu<128, C>();
+    case 256: return wgs_per_cu<256, C>();
   }
   return 0;
 }
