@@ -116,22 +116,9 @@ void fwd_fp8(Fp8Params p) {
   const int qrow0 = qt * BR + w * 32;
   const int myq = qrow0 + ql;
 
-  // Q operand (B of S^T = K Q^T): lane holds Q8[myq][64 s + 32 g .. +32].
-  // A negative scale is moved into Q (flip the e4m3 sign bits, exact).
+  // Q operand (B of S^T = K Q^T): lane holds Q8[myq][64 s + 32 g .. +32];
+  // loaded after the first tile copies are issued (below).
   i32x8 qop[NS];
-  {
-    const uint8_t* qr = qh + (size_t)min(myq, N - 1) * D + 32 * g;
-    const int flip = p.scale_log2 < 0.f ? (int)0x80808080u : 0;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const i32x4 lo = *(const i32x4*)(qr + 64 * s), hi = *(const i32x4*)(qr + 64 * s + 16);
-      qop[s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qop[s][e] ^= flip;
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qop[s]));  // drain before the copies
-  }
   const float c = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
   const float cq = c * qd[qt];  // the workgroup's 128 rows are one descale block
 
@@ -181,7 +168,23 @@ void fwd_fp8(Fp8Params p) {
   // iteration t - PD - 1.  Copies complete in order: "tile j + 1 has landed"
   // is vmcnt <= 2 CPT x (tiles issued after it).
   for (int t = 0; t < PD && t < nt; ++t) issue_tile(t);
-  wait_vmcnt(2 * CPT * (min(nt, PD) - 1));
+  // The first tiles are issued before Q is read, so that both latencies
+  // overlap; Q's loads are the newest, and draining them drains the copies.
+  // A negative scale is moved into Q (flip the e4m3 sign bits, exact).
+  {
+    const uint8_t* qr = qh + (size_t)min(myq, N - 1) * D + 32 * g;
+    const int flip = p.scale_log2 < 0.f ? (int)0x80808080u : 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const i32x4 lo = *(const i32x4*)(qr + 64 * s), hi = *(const i32x4*)(qr + 64 * s + 16);
+      qop[s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qop[s][e] ^= flip;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qop[s]));
+  }
+  wait_vmcnt(0);
   __syncthreads();
 
   for (int j = 0; j < nt; ++j) {
@@ -302,21 +305,33 @@ void fwd_fp8(Fp8Params p) {
   }
 
   // ---- epilogue: O = O~ 2^(lazy - 8) / l, LSE = ln2 (m + log2 l) ----
+  // A lane holds one query's O row in 8-byte pieces; each wave stages its 32
+  // bf16 rows in LDS (the ring is idle after the last barrier) and writes
+  // whole 256-byte rows, 16-byte chunks XOR-swizzled by row.
+  constexpr int ORB = D * 2, OCPR = ORB / 16;
+  static_assert(NW * 32 * ORB <= ST * SB, "staging fits in the ring");
+  char* stg = smem + w * (32 * ORB);
   const float lt = pair_sum(l);
-  if (myq < N) {
-    const float inv = __builtin_amdgcn_exp2f(kLazy8 - 8.0f) / lt;
-    __bf16* orow = (__bf16*)p.o + head + (size_t)myq * D;
+  const float inv = __builtin_amdgcn_exp2f(kLazy8 - 8.0f) / lt;
 #pragma unroll
-    for (int b = 0; b < ND; ++b)
+  for (int b = 0; b < ND; ++b)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        uint2 stv;
-        stv.x = pack_bf16x2(oacc[b][4 * a] * inv, oacc[b][4 * a + 1] * inv);
-        stv.y = pack_bf16x2(oacc[b][4 * a + 2] * inv, oacc[b][4 * a + 3] * inv);
-        *(uint2*)(orow + 32 * b + 8 * a + 4 * g) = stv;
-      }
-    if (g == 0)
-      p.lse[(size_t)bh * N + myq] = (m + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+    for (int a = 0; a < 4; ++a) {
+      uint2 stv;
+      stv.x = pack_bf16x2(oacc[b][4 * a] * inv, oacc[b][4 * a + 1] * inv);
+      stv.y = pack_bf16x2(oacc[b][4 * a + 2] * inv, oacc[b][4 * a + 3] * inv);
+      *(uint2*)(stg + ql * ORB + (((4 * b + a) ^ (ql & (OCPR - 1))) << 4) + 8 * g) = stv;
+    }
+  if (g == 0 && myq < N)
+    p.lse[(size_t)bh * N + myq] = (m + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are staged
+  __bf16* __restrict__ oh = (__bf16*)p.o + head;
+#pragma unroll
+  for (int it = 0; it < 32 * OCPR / 64; ++it) {
+    const int idx = it * 64 + lane, row = idx / OCPR, ch = idx % OCPR;
+    const i32x4 val = *(const i32x4*)(stg + row * ORB + ((ch ^ (row & (OCPR - 1))) << 4));
+    const int grow = qrow0 + row;
+    if (grow < N) *(i32x4*)(oh + (size_t)grow * D + ch * 8) = val;
   }
 }
 
