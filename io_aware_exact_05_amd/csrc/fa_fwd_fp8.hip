@@ -5,10 +5,11 @@
 // 8-bit floats, v_mfma_scale_f32_32x32x64_f8f6f4 at twice the bf16 rate, with
 // per-128-row fp32 descales for Q, K and V.
 //
-// Same tiling and online softmax as the 16-bit kernel: one workgroup owns
-// 128 query rows (four waves of 32, one descale block), K/V tiles of 128
-// rows (one descale block each) stream through an LDS ring filled by direct
-// global -> LDS copies; S^T = K8 Q8^T keeps one query per lane.
+// Same tiling and online softmax as the 16-bit kernel: each wave owns 32
+// query rows (within one descale block), a workgroup of 8 (4 with causal
+// masking) waves 256 (128) rows; K/V tiles of 128 rows (one descale block
+// each) stream through an LDS ring filled by direct global -> LDS copies;
+// S^T = K8 Q8^T keeps one query per lane.
 //   scores    t = s8 * (scale log2 e * q_descale[query block] *
 //             k_descale[tile]): one per-tile multiplier folded into the FMA.
 //   V descale each tile's descale is split as v_descale = 2^e f with f in
@@ -69,23 +70,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Key-tile rows (64 or 128), ring stages and waves per SIMD (tuning builds
-// may override them).  Measured: 128-key tiles in a 2-stage ring at two waves
-// per SIMD beat 64-key tiles at two waves (about 12%) and at three (spills).
+// Key-tile rows (64 or 128) and waves per SIMD (tuning builds may override
+// them).  Measured: 128-key tiles beat 64-key tiles (about 12%).  Waves per
+// workgroup NW: 8 without masking (the two halves of the workgroup, waves w
+// and w + 4 sharing a SIMD, run half a tile apart: +5%), 4 with causal
+// masking (more, smaller workgroups balance the unequal causal tiles).
 #ifndef FA_FP8_BC
 #define FA_FP8_BC 128
-#endif
-#ifndef FA_FP8_ST
-#define FA_FP8_ST 2
 #endif
 #ifndef FA_FP8_OCC
 #define FA_FP8_OCC 2
 #endif
+template <bool CAUSAL> constexpr int fp8_nw() { return CAUSAL ? 4 : 8; }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FP8_OCC, FA_FP8_OCC)))
+__global__ __launch_bounds__(64 * fp8_nw<CAUSAL>()) __attribute__((amdgpu_waves_per_eu(FA_FP8_OCC, FA_FP8_OCC)))
 void fwd_fp8(Fp8Params p) {
-  constexpr int D = 128, BC = FA_FP8_BC, NW = 4, BR = 32 * NW, ST = FA_FP8_ST, PD = ST - 1;
+  constexpr int NW = fp8_nw<CAUSAL>();
+  constexpr int D = 128, BC = FA_FP8_BC, BR = 32 * NW, ST = NW == 8 ? 4 : 2;
+  constexpr bool PP = NW == 8;
+  constexpr int PD = PP ? ST - 2 : ST - 1;   // tiles copied ahead
   constexpr int RB = D;                      // bytes per fp8 row
   constexpr int TB = BC * RB;                // bytes per K or V tile
   constexpr int SB = 2 * TB;                 // ring stage: K tile, then V tile
@@ -95,12 +99,14 @@ void fwd_fp8(Fp8Params p) {
   constexpr int NKB = BC / 32;               // 32-key blocks per tile
   constexpr int NKS = BC / 64;               // MFMA k-steps of V^T P^T
   constexpr int ND = D / 32;                 // 32-column blocks of O
-  static_assert((BC == 64 || BC == 128) && BR == 128,
-                "query tiles are one 128-row descale block, key tiles a half or whole one");
+  static_assert((BC == 64 || BC == 128) && BR % 128 == 0,
+                "query tiles are whole 128-row descale blocks, key tiles a half or whole one");
+  static_assert(CPT * 64 * NW == BC * CPR, "tile must split evenly over the waves");
   static_assert(PD >= 1 && 2 * CPT * (PD - 1) <= 31, "ring depth");
   __shared__ __attribute__((aligned(1024))) char smem[ST * SB];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, g = lane >> 5;
   const int N = p.N;
   int bh, qt;
@@ -120,11 +126,14 @@ void fwd_fp8(Fp8Params p) {
   // loaded after the first tile copies are issued (below).
   i32x8 qop[NS];
   const float c = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
-  const float cq = c * qd[qt];  // the workgroup's 128 rows are one descale block
+  // this wave's 32 rows lie in one 128-row descale block (rows past N use
+  // the last block: their results are not stored)
+  const float cq = c * qd[min(qrow0, N - 1) >> 7];
 
   const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
   const int nt = (kv_end + BC - 1) / BC;
-  const int jlast = CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1;
+  // last tile this wave computes (-1: all its rows are past N)
+  const int jlast = qrow0 >= N ? -1 : (CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1);
 
   // ---- copies (as in the 16-bit kernel, 128-byte rows) ----
   int ld_row[CPT], ld_off[CPT];
@@ -135,7 +144,7 @@ void fwd_fp8(Fp8Params p) {
     ld_off[u] = (ch16 ^ swz8(row)) * 16;
   }
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
-  auto issue_tile = [&](int j) {
+  auto issue_tile = [&](int j) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + (j % ST) * SB + w * 1024;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
@@ -163,15 +172,127 @@ void fwd_fp8(Fp8Params p) {
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float m = kMInit, l = 0.f;
 
+  // ---- S^T = K8 Q8^T for tile j (stage st) ----
+  auto qk = [&](int st, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
+    const char* sk = smem + st * SB;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const char* kr = sk + (kb * 32 + krow) * RB;
+        const i32x4 lo = *(const i32x4*)(kr + (((4 * s + 2 * g) ^ kx) << 4));
+        const i32x4 hi = *(const i32x4*)(kr + (((4 * s + 2 * g + 1) ^ kx) << 4));
+        S[kb] = mfma8(i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, qop[s], S[kb]);
+      }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- scale, mask, online softmax of tile j; P~ packed to e4m3 ----
+  // Rescales O when the running max moves; returns the tile's V scale (E8M0).
+  auto softmax = [&](int j, f32x16 (&S)[NKB], i32x8 (&P)[NKS]) __attribute__((always_inline)) -> int {
+    const int key0 = j * BC;
+    const int blk = (j * BC) >> 7;  // the 128-row descale block of tile j
+    const float ct = cq * kd[blk];
+    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qrow0)) {
+      const int lim = CAUSAL ? min(myq, N - 1) : N - 1;
+      const int rel = lim - key0 - 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          S[kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) <= rel) ? S[kb][r] : kNegInf;
+    }
+    float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], S[kb][r]);
+    const float mx = pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
+    const float mt = (mx == kNegInf) ? kNegInf : mx * ct;
+    const bool upd = mt > m + kLazy8;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      const float mnew = upd ? mt : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < ND; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    }
+    // v_descale = 2^e f, f in (1/2, 1]; the E8M0 scale 127 + e is kept in
+    // [0, 254] (255 encodes NaN)
+    const float vdj = vd[blk];
+    int ex = __builtin_amdgcn_frexp_expf(vdj);
+    const float mant = __builtin_amdgcn_frexp_mantf(vdj);  // [1/2, 1)
+    const float f = (mant == 0.5f) ? 1.0f : mant;
+    ex -= (mant == 0.5f) ? 1 : 0;
+    const float beta = (8.0f - kLazy8) + __builtin_amdgcn_logf(f) - m;
+    const float lsc = __builtin_amdgcn_exp2f(kLazy8 - 8.0f) / f;
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], ct, beta));
+        S[kb][r] = pr;
+        rs4[r & 3] += pr;
+      }
+    l += ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3])) * lsc;
+    // P~ operand of k-step ks: bytes 16 kbh + 8 h + e <- S[2 ks + kbh][8 h + e]
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kbh = 0; kbh < 2; ++kbh)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int q4 = 0; q4 < 2; ++q4) {
+            const f32x16& sv16 = S[2 * ks + kbh];
+            const int r0 = 8 * h + 4 * q4;
+            P[ks][4 * kbh + 2 * h + q4] =
+                (int)pack4_e4m3(sv16[r0], sv16[r0 + 1], sv16[r0 + 2], sv16[r0 + 3]);
+          }
+    return min(max(127 + ex, 0), 254);
+  };
+
+  // ---- O^T += V8^T P~^T for the tile in stage st, V scale sa ----
+  auto pv = [&](int st, const i32x8 (&P)[NKS], int sa) __attribute__((always_inline)) {
+    const char* sv = smem + st * SB + TB;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int b = 0; b < ND; ++b) {
+        i32x2 part[4];
+#pragma unroll
+        for (int kbh = 0; kbh < 2; ++kbh)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const char* a = sv + (32 * (2 * ks + kbh) + 16 * h) * RB + vrow_off + (((2 * b) ^ vx) << 4);
+            part[2 * kbh + h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
+          }
+        const i32x8 va = {part[0][0], part[0][1], part[1][0], part[1][1],
+                          part[2][0], part[2][1], part[3][0], part[3][1]};
+        oacc[b] = mfma8_sa(va, P[ks], oacc[b], sa);
+      }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
   // Ring of ST stages: tile t is copied during iteration t - PD into the stage
   // of tile t - ST, which every wave finished before the barrier that ended
-  // iteration t - PD - 1.  Copies complete in order: "tile j + 1 has landed"
-  // is vmcnt <= 2 CPT x (tiles issued after it).
-  for (int t = 0; t < PD && t < nt; ++t) issue_tile(t);
+  // iteration t - PD - 1 (with ping-pong halves the upper half reads tile
+  // j - 1 in iteration j, hence PD = ST - 2).  Copies complete in order:
+  // "tile j + 1 has landed" is vmcnt <= 2 CPT x (tiles issued after it).
   // The first tiles are issued before Q is read, so that both latencies
   // overlap; Q's loads are the newest, and draining them drains the copies.
-  // A negative scale is moved into Q (flip the e4m3 sign bits, exact).
-  {
+  for (int t = 0; t < PD && t < nt; ++t) issue_tile(t);
+  {  // a negative scale is moved into Q (flip the e4m3 sign bits, exact)
     const uint8_t* qr = qh + (size_t)min(myq, N - 1) * D + 32 * g;
     const int flip = p.scale_log2 < 0.f ? (int)0x80808080u : 0;
 #pragma unroll
@@ -187,114 +308,28 @@ void fwd_fp8(Fp8Params p) {
   wait_vmcnt(0);
   __syncthreads();
 
-  for (int j = 0; j < nt; ++j) {
+  // Lower half (and 4-wave workgroups): scores, softmax and P V of tile j.
+  // Upper half of an 8-wave workgroup: P V of tile j - 1, then scores and
+  // softmax of tile j; its packed P~ and V scale wait across the barrier.
+  const bool upper = PP && w >= NW / 2;
+  f32x16 S[NKB];
+  i32x8 P[NKS];
+  int sa = 127;
+  auto step = [&](int j, auto LAG) __attribute__((always_inline)) {
     const int st = j % ST;
     if (j + PD < nt) issue_tile(j + PD);
-    if (j <= jlast) {
-      const char* sk = smem + st * SB;
-      const char* sv = sk + TB;
-      // ---- S^T = K8 Q8^T ----
-      f32x16 S[NKB];
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const char* kr = sk + (kb * 32 + krow) * RB;
-          const i32x4 lo = *(const i32x4*)(kr + (((4 * s + 2 * g) ^ kx) << 4));
-          const i32x4 hi = *(const i32x4*)(kr + (((4 * s + 2 * g + 1) ^ kx) << 4));
-          S[kb] = mfma8(i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, qop[s], S[kb]);
-        }
-      __builtin_amdgcn_s_setprio(0);
-      // ---- scale, mask, online softmax ----
-      const int key0 = j * BC;
-      const int blk = (j * BC) >> 7;  // the 128-row descale block of tile j
-      const float ct = cq * kd[blk];
-      if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qrow0)) {
-        const int lim = CAUSAL ? min(myq, N - 1) : N - 1;
-        const int rel = lim - key0 - 8 * g;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            S[kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) <= rel) ? S[kb][r] : kNegInf;
+    if constexpr (!decltype(LAG)::value) {
+      if (j <= jlast) {
+        qk(st, S);
+        sa = softmax(j, S, P);
+        pv(st, P, sa);
       }
-      float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], S[kb][r]);
-      const float mx = pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
-      const float mt = (mx == kNegInf) ? kNegInf : mx * ct;
-      const bool upd = mt > m + kLazy8;
-      if (__builtin_amdgcn_ballot_w64(upd)) {
-        const float mnew = upd ? mt : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
-        l *= alpha;
-#pragma unroll
-        for (int b = 0; b < ND; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    } else {
+      if (j >= 1 && j - 1 <= jlast) pv((j + ST - 1) % ST, P, sa);
+      if (j <= jlast) {
+        qk(st, S);
+        sa = softmax(j, S, P);
       }
-      // v_descale = 2^e f, f in (1/2, 1]; the E8M0 scale 127 + e is kept in
-      // [0, 254] (255 encodes NaN)
-      const float vdj = vd[blk];
-      int ex = __builtin_amdgcn_frexp_expf(vdj);
-      const float mant = __builtin_amdgcn_frexp_mantf(vdj);  // [1/2, 1)
-      const float f = (mant == 0.5f) ? 1.0f : mant;
-      ex -= (mant == 0.5f) ? 1 : 0;
-      const int sa = min(max(127 + ex, 0), 254);
-      const float beta = (8.0f - kLazy8) + __builtin_amdgcn_logf(f) - m;
-      const float lsc = __builtin_amdgcn_exp2f(kLazy8 - 8.0f) / f;
-      float rs4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], ct, beta));
-          S[kb][r] = pr;
-          rs4[r & 3] += pr;
-        }
-      l += ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3])) * lsc;
-      // ---- O^T += V8^T P~^T ----
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        // P~ operand: bytes 16 kbh + 8 h + e <- S[2 ks + kbh][8 h + e]
-        i32x8 pop;
-#pragma unroll
-        for (int kbh = 0; kbh < 2; ++kbh)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int q4 = 0; q4 < 2; ++q4) {
-              const f32x16& sv16 = S[2 * ks + kbh];
-              const int r0 = 8 * h + 4 * q4;
-              pop[4 * kbh + 2 * h + q4] =
-                  (int)pack4_e4m3(sv16[r0], sv16[r0 + 1], sv16[r0 + 2], sv16[r0 + 3]);
-            }
-#pragma unroll
-        for (int b = 0; b < ND; ++b) {
-          i32x2 part[4];
-#pragma unroll
-          for (int kbh = 0; kbh < 2; ++kbh)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const char* a = sv + (32 * (2 * ks + kbh) + 16 * h) * RB + vrow_off +
-                              (((2 * b) ^ vx) << 4);
-              part[2 * kbh + h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
-            }
-          const i32x8 va = {part[0][0], part[0][1], part[1][0], part[1][1],
-                            part[2][0], part[2][1], part[3][0], part[3][1]};
-          oacc[b] = mfma8_sa(va, pop, oacc[b], sa);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
     }
     if (j + PD < nt) {  // steady state: tiles j + 2 .. j + PD may stay in flight
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPT * (PD - 1)) : "memory");
@@ -302,6 +337,14 @@ void fwd_fp8(Fp8Params p) {
       wait_vmcnt(2 * CPT * max(0, nt - 1 - (j + 1)));
     }
     __syncthreads();
+  };
+  // With ping-pong halves both run one extra iteration (j = nt): the upper
+  // half does its last P V there, the lower half only meets the barrier.
+  const int nsteps = PP ? nt + 1 : nt;
+  if (upper) {
+    for (int j = 0; j < nsteps; ++j) step(j, std::true_type());
+  } else {
+    for (int j = 0; j < nsteps; ++j) step(j, std::false_type());
   }
 
   // ---- epilogue: O = O~ 2^(lazy - 8) / l, LSE = ln2 (m + log2 l) ----
@@ -339,13 +382,14 @@ void fwd_fp8(Fp8Params p) {
 
 hipError_t launch_fwd_fp8(const Fp8Params& p, int d, int causal, hipStream_t s) {
   if (d != 128) return hipErrorInvalidValue;
+  const int nw = causal ? fp8_nw<true>() : fp8_nw<false>();
   Fp8Params q = p;
-  q.nq = (p.N + 127) / 128;
+  q.nq = (p.N + 32 * nw - 1) / (32 * nw);
   const unsigned grid = (unsigned)(q.nq * p.BH);
   if (causal)
-    hipLaunchKernelGGL((fwd_fp8<true>), dim3(grid), dim3(256), 0, s, q);
+    hipLaunchKernelGGL((fwd_fp8<true>), dim3(grid), dim3(64 * nw), 0, s, q);
   else
-    hipLaunchKernelGGL((fwd_fp8<false>), dim3(grid), dim3(256), 0, s, q);
+    hipLaunchKernelGGL((fwd_fp8<false>), dim3(grid), dim3(64 * nw), 0, s, q);
   return hipGetLastError();
 }
 
