@@ -135,6 +135,7 @@ def main():
     # Each entry of `parts` is one launch of the step: (name, workload or None
     # for a quantiser launch, callable).  Every buffer is allocated here.
     data, parts = [], []
+    multi_d = len({w.d for w in cases}) > 1
     for w in cases:
         q, k, v = inputs.workload_inputs(w)
         qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
@@ -142,7 +143,8 @@ def main():
         data.append((w, (q, k, v)))
         if not fp8:
             o = torch.empty_like(qd)
-            parts.append(("causal" if w.causal else "noncausal", w,
+            name = ("causal" if w.causal else "noncausal") + (f"_d{w.d}" if multi_d else "")
+            parts.append((name, w,
                           lambda w=w, t=(qd, kd, vd, o, lse):
                           fa.fa_fwd(*t, bool(w.causal), w.scale, stream)))
             continue

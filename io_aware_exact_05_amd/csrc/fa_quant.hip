@@ -19,7 +19,11 @@
 // One workgroup (256 threads) per block: thread t holds half of row t / 2
 // in registers; the last butterfly stage of the transform pairs the two
 // halves across neighbouring lanes.  The pass is bound by HBM traffic:
-// 4 bytes read and 1 byte written per element.
+// 4 bytes read and 1 byte written per element.  For d <= 128 the block
+// moves through LDS both ways, so that every global access instruction
+// covers whole contiguous rows: the fp32 rows arrive by direct global -> LDS
+// copies (16-byte chunks XOR-swizzled within each half row), and the codes
+// are staged row-major before 16-byte stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,9 +34,21 @@ namespace {
 
 constexpr int kBlockRows = 128;
 
+// 16-byte buffer -> LDS copy per lane (lane i's bytes land at lds_addr + 16 i;
+// offsets past the resource read zeros); the caller waits on vmcnt.
+__device__ __forceinline__ void q_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
 template <int D, bool ROT>
 __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
   constexpr int E = D / 2;  // elements per thread (half a row)
+  constexpr bool STAGE = D <= 128;  // LDS holds the 128 fp32 rows
+  constexpr int RB = D * 4, CPR = RB / 16, HC = CPR / 2;  // row bytes, chunks per row, per half
+  __shared__ __attribute__((aligned(1024))) char tile[STAGE ? kBlockRows * RB : 16];
   const int t = threadIdx.x, r = t >> 1, hf = t & 1;
   const int bh = blockIdx.x / p.nblk, blk = blockIdx.x % p.nblk;
   const int row = blk * kBlockRows + r;
@@ -40,7 +56,38 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
   const size_t base = ((size_t)bh * p.N + (valid ? row : 0)) * D + hf * E;
 
   float x[E];
-  if (valid) {
+  if constexpr (STAGE) {
+    // slot s of the tile (row s / CPR, position s % CPR) receives chunk
+    // position ^ (row % HC) of that row; rows past N read as zeros
+    const size_t blk_elem = ((size_t)bh * p.N + (size_t)blk * kBlockRows) * D;
+    const int rows_left = min(kBlockRows, p.N - blk * kBlockRows);
+    // base address made wave-uniform word by word; each word stays unsigned
+    // (readfirstlane returns int, which must not be sign-extended)
+    const uint64_t a = (uint64_t)(uintptr_t)(p.x + blk_elem);
+    const uint32_t a_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t a_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* ub = (void*)(uintptr_t)(((uint64_t)a_hi << 32) | (uint64_t)a_lo);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        ub, 0, (int)__builtin_amdgcn_readfirstlane((uint32_t)(rows_left * RB)), 0x00020000);
+    const int w = t >> 6, lane = t & 63;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)tile;
+    constexpr int NI = kBlockRows * CPR / 256;  // copies per thread
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int sl = (u * 4 + w) * 64 + lane, rr = sl / CPR, pos = sl % CPR;
+      q_dma16(rs, (uint32_t)(rr * RB + ((pos ^ (rr % HC)) << 4)), lds0 + (u * 4 + w) * 1024);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < HC; ++k) {
+      const float4 v = *(const float4*)(tile + r * RB + ((hf * HC + (k ^ (r % HC))) << 4));
+      x[4 * k] = v.x;
+      x[4 * k + 1] = v.y;
+      x[4 * k + 2] = v.z;
+      x[4 * k + 3] = v.w;
+    }
+  } else if (valid) {
     const float4* src = (const float4*)(p.x + base);
 #pragma unroll
     for (int i = 0; i < E / 4; ++i) {
@@ -98,18 +145,36 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
   if (t == 0) p.descale[(size_t)bh * p.nblk + blk] = zero ? 1.0f : __builtin_amdgcn_ldexpf(1.0f, e);
   const int ne = zero ? 0 : -e;  // x 2^-e by exponent arithmetic (exact)
 
-  if (valid) {
-    uint32_t packed[E / 4];
+  uint32_t packed[E / 4];
 #pragma unroll
-    for (int i = 0; i < E / 4; ++i) {
-      float v[4];
+  for (int i = 0; i < E / 4; ++i) {
+    float v[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        v[k] = fminf(fmaxf(__builtin_amdgcn_ldexpf(x[4 * i + k], ne), -448.0f), 448.0f);
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
-      packed[i] = (uint32_t)w;
+    for (int k = 0; k < 4; ++k)
+      v[k] = fminf(fmaxf(__builtin_amdgcn_ldexpf(x[4 * i + k], ne), -448.0f), 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+    packed[i] = (uint32_t)w;
+  }
+  if constexpr (STAGE) {
+    // codes row-major in LDS (D bytes per row; the 16-byte chunks of a row
+    // XOR-swizzled by row), then 16-byte stores of whole rows
+    constexpr int CR = D / 16, HCR = CR / 2;  // code chunks per row and per half
+    __syncthreads();  // every thread has read its fp32 half row
+#pragma unroll
+    for (int i = 0; i < E / 16; ++i)
+      *(uint4*)(tile + r * D + ((hf * HCR + (i ^ (r % HCR))) << 4)) =
+          make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+    __syncthreads();
+    const int rows_left = min(kBlockRows, p.N - blk * kBlockRows);
+    uint8_t* dst = p.x8 + ((size_t)bh * p.N + (size_t)blk * kBlockRows) * D;
+#pragma unroll
+    for (int u = 0; u < kBlockRows * CR / 256; ++u) {
+      const int sl = u * 256 + t, rr = sl / CR, c = sl % CR;
+      const uint4 val = *(const uint4*)(tile + rr * D + (((c & ~(HCR - 1)) | ((c ^ (rr % HCR)) & (HCR - 1))) << 4));
+      if (rr < rows_left) *(uint4*)(dst + (size_t)rr * D + c * 16) = val;
     }
+  } else if (valid) {
     uint4* dst = (uint4*)(p.x8 + base);
 #pragma unroll
     for (int i = 0; i < E / 16; ++i)
