@@ -67,7 +67,7 @@ namespace fa {
 // Which head dimensions run fwd_wide (fa_fwd_wide.hip) instead of the kernel
 // below (see use_wide for the causal case).
 #ifndef FA_D64_WIDE
-#define FA_D64_WIDE 0
+#define FA_D64_WIDE 1
 #endif
 #ifndef FA_D128_WIDE
 #define FA_D128_WIDE 1

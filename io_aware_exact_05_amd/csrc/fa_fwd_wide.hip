@@ -71,12 +71,14 @@ constexpr bool swz_step4_is_xor1() {
 //           3.5-5% over two uncoordinated 4-wave workgroups);
 //   d = 128 causal: 32 rows per wave at three waves per SIMD (twice as many
 //           workgroups, so the unequal causal tiles balance over rounds);
-//   d = 256: 32 rows per wave, two waves per SIMD.
-// d = 64 runs the 8-wave kernel (no gain measured here); its entry is kept.
+//   d = 256: 32 rows per wave, two waves per SIMD;
+//   d = 64: 64 rows per wave and 64-key tiles (the state is small), one
+//           8-wave workgroup per CU with ping-pong halves (+10-12% over the
+//           32-row 8-wave kernel).
 template <int D, bool CAUSAL> struct WideCfg;
 template <bool C> struct WideCfg<64, C> {
-  static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2;
-  static constexpr bool XK = true, XV = true;
+  static constexpr int QB = 2, BC = 64, ST = 3, OCC = 2, NW = 8;
+  static constexpr bool XK = false, XV = false;
 };
 template <> struct WideCfg<128, false> {
   static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2, NW = 8;
@@ -153,7 +155,7 @@ void fwd_wide(FwdParams p) {
   const __amdgpu_buffer_rsrc_t kbuf = make_rsrc(kh, head_bytes);
   const __amdgpu_buffer_rsrc_t vbuf = make_rsrc(vh, head_bytes);
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
-  auto issue_tile = [&](int j) {
+  auto issue_tile = [&](int j) __attribute__((always_inline)) {
     const uint32_t kdst = smem_base + (j % ST) * 2 * TB + w * 1024;
     const uint32_t t0 = (uint32_t)j * TB;
 #pragma unroll
@@ -205,7 +207,7 @@ void fwd_wide(FwdParams p) {
 
   // S^T = K_j Q^T for both query blocks; each K operand read feeds two MFMAs
   // (the first k-step starts from a zero accumulator).  SG = stage of tile j.
-  auto qk = [&](auto SG, STile& S) {
+  auto qk = [&](auto SG, STile& S) __attribute__((always_inline)) {
     const char* sk = smem + decltype(SG)::value * 2 * TB;
     const f32x16 zero = {};
     // With XK the per-step addresses are formed here, not hoisted out of the
@@ -229,7 +231,7 @@ void fwd_wide(FwdParams p) {
   };
 
   // Hidden keys of tile j become -inf (tiles crossing the diagonal or N).
-  auto mask = [&](int j, STile& S) {
+  auto mask = [&](int j, STile& S) __attribute__((always_inline)) {
     const int key0 = j * BC;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -242,13 +244,13 @@ void fwd_wide(FwdParams p) {
           S[qb][kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) <= rel) ? S[qb][kb][r] : kNegInf;
     }
   };
-  auto needs_mask = [&](int j) {
+  auto needs_mask = [&](int j) __attribute__((always_inline)) {
     return (j * BC + BC > N) || (CAUSAL && j * BC + BC - 1 > qrow0);
   };
 
   // Online softmax of S (branch-free): running max with lazy moves, P packed
   // to 16-bit for the second product, alpha = factor O must be scaled by.
-  auto softmax = [&](STile& S, PTile& P, float (&alpha)[QB]) {
+  auto softmax = [&](STile& S, PTile& P, float (&alpha)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // four independent chains, started from the first four scores
@@ -285,7 +287,7 @@ void fwd_wide(FwdParams p) {
     }
   };
 
-  auto rescale = [&](const float (&alpha)[QB]) {
+  auto rescale = [&](const float (&alpha)[QB]) __attribute__((always_inline)) {
     bool any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) any = any || alpha[qb] != 1.0f;
@@ -300,7 +302,7 @@ void fwd_wide(FwdParams p) {
   };
 
   // O^T += V_j^T P^T; each V operand read feeds both query blocks.
-  auto pv = [&](auto SG, const PTile& P) {
+  auto pv = [&](auto SG, const PTile& P) __attribute__((always_inline)) {
     const char* sv = smem + decltype(SG)::value * 2 * TB + TB;
     int va0 = vaddr;
     if constexpr (Cfg::XV) asm volatile("" : "+v"(va0));  // as in qk
@@ -475,12 +477,16 @@ hipError_t launch_wide_t(const FwdParams& p, int d, int causal, hipStream_t s) {
 
 }  // namespace
 
+template <int D, bool C>
+static constexpr int rows_of() {
+  return 32 * NWOf<WideCfg<D, C>>::v * WideCfg<D, C>::QB;
+}
 template <bool C>
 static int rows_per_block(int d) {
   switch (d) {
-    case 64: return 128 * WideCfg<64, C>::QB;
-    case 128: return 32 * NWOf<WideCfg<128, C>>::v * WideCfg<128, C>::QB;
-    case 256: return 128 * WideCfg<256, C>::QB;
+    case 64: return rows_of<64, C>();
+    case 128: return rows_of<128, C>();
+    case 256: return rows_of<256, C>();
   }
   return 0;
 }

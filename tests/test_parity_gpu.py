@@ -59,14 +59,15 @@ def test_small_shapes_every_element(dtype, d, N, causal):
         assert st["o_max_abs"] < 1e-4 and st["lse_max_abs"] < 1e-4, st
 
 
-# d = 128 and d = 256 have two kernels each: causal launches whose grid fits
-# in one round of the one-wave-per-SIMD kernel's slots (three 128-row
-# workgroups per CU at d = 128, two at d = 256) go to the 8-wave kernel, all
-# others to the former.  The small shapes above take the first route for
-# causal masking; these head counts push small, ragged causal launches past
-# 768 workgroups so the second kernel is checked element by element too.
+# Each head dimension has two kernels: causal launches whose grid fits in one
+# round of the wide kernel's workgroup slots (one 512-row workgroup per CU at
+# d = 64, three 128-row ones at d = 128, two at d = 256) go to the 8-wave
+# 32-row kernel, all others to the former.  The small shapes above take the
+# first route for causal masking; these head counts push small, ragged causal
+# launches past 768 workgroups so the wide kernel is checked element by
+# element too.
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("BH,N", [(800, 100), (400, 300), (260, 257)])
 def test_many_heads_causal_every_element(dtype, d, BH, N):
     _say(f"case many-heads causal dtype={dtype} d={d} BH={BH} N={N}")
