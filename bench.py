@@ -78,7 +78,7 @@ def kernel_name(w) -> str:
         return "fwd_f32"
     # rows per workgroup and workgroups per CU of the one-wave-per-SIMD kernel
     rows, per_cu = {(64, 0): (512, 1), (64, 1): (512, 1), (128, 0): (512, 1), (128, 1): (128, 3),
-                    (256, 0): (128, 2), (256, 1): (128, 2)}.get((w.d, w.causal), (0, 0))
+                    (256, 0): (256, 1), (256, 1): (256, 1)}.get((w.d, w.causal), (0, 0))
     if rows and (not w.causal or (w.N + rows - 1) // rows * w.B * w.H > per_cu * 256):
         return "fwd_wide"
     return "fwd_mfma16"

@@ -71,7 +71,8 @@ constexpr bool swz_step4_is_xor1() {
 //           3.5-5% over two uncoordinated 4-wave workgroups);
 //   d = 128 causal: 32 rows per wave at three waves per SIMD (twice as many
 //           workgroups, so the unequal causal tiles balance over rounds);
-//   d = 256: 32 rows per wave, two waves per SIMD;
+//   d = 256: 32 rows per wave, one 8-wave workgroup per CU with ping-pong
+//           halves (+1-2% over two 4-wave workgroups);
 //   d = 64: 64 rows per wave and 64-key tiles (the state is small), one
 //           8-wave workgroup per CU with ping-pong halves (+10-12% over the
 //           32-row 8-wave kernel).
@@ -89,7 +90,7 @@ template <> struct WideCfg<128, true> {
   static constexpr bool XK = false, XV = false;
 };
 template <bool C> struct WideCfg<256, C> {
-  static constexpr int QB = 1, BC = 32, ST = 2, OCC = 2;
+  static constexpr int QB = 1, BC = 32, ST = 4, OCC = 2, NW = 8;
   static constexpr bool XK = true, XV = true;
 };
 

@@ -61,7 +61,7 @@ def test_small_shapes_every_element(dtype, d, N, causal):
 
 # Each head dimension has two kernels: causal launches whose grid fits in one
 # round of the wide kernel's workgroup slots (one 512-row workgroup per CU at
-# d = 64, three 128-row ones at d = 128, two at d = 256) go to the 8-wave
+# d = 64, three 128-row ones at d = 128, one 256-row one at d = 256) go to the 8-wave
 # 32-row kernel, all others to the former.  The small shapes above take the
 # first route for causal masking; these head counts push small, ragged causal
 # launches past 768 workgroups so the wide kernel is checked element by
