@@ -103,8 +103,14 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
   }
 
   if constexpr (ROT) {
+    // column factors signs[c] / sqrt(d), read once per workgroup into LDS
+    // (all lanes of a half then read the same words: broadcast)
+    __shared__ __attribute__((aligned(16))) float colf[D];
+    if (t < D) colf[t] = (p.signs ? p.signs[t] : 1.0f) * p.inv_sqrt_d;
     // Walsh-Hadamard butterflies (a, b) -> (a + b, a - b) at strides 1 .. E/2
-    // inside the thread, then stride E across the lane pair.
+    // inside the thread, then stride E across the lane pair: the lower lane
+    // keeps a + b, the upper one a - b = o - x (o = the partner's value,
+    // fetched by a DPP quad permutation [1, 0, 3, 2]).
 #pragma unroll
     for (int h = 1; h < E; h <<= 1)
 #pragma unroll
@@ -114,16 +120,21 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
           x[i] = a + b;
           x[i + h] = a - b;
         }
+    const float sx = hf ? -1.0f : 1.0f;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const float o = __shfl_xor(x[i], 1);
-      x[i] = hf ? (o - x[i]) : (x[i] + o);
+      const float o = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[i]), 0xB1, 0xF, 0xF, false));
+      x[i] = __builtin_fmaf(sx, x[i], o);
     }
-    const float inv_sqrt_d = p.inv_sqrt_d;
+    __syncthreads();  // colf written
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const float s = p.signs ? p.signs[hf * E + i] : 1.0f;
-      x[i] = x[i] * (s * inv_sqrt_d);
+    for (int i = 0; i < E / 4; ++i) {
+      const float4 f4 = *(const float4*)(colf + hf * E + 4 * i);
+      x[4 * i] *= f4.x;
+      x[4 * i + 1] *= f4.y;
+      x[4 * i + 2] *= f4.z;
+      x[4 * i + 3] *= f4.w;
     }
   }
 
