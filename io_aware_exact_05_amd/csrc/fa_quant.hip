@@ -22,8 +22,9 @@
 // 4 bytes read and 1 byte written per element.  For d <= 128 the block
 // moves through LDS both ways, so that every global access instruction
 // covers whole contiguous rows: the fp32 rows arrive by direct global -> LDS
-// copies (16-byte chunks XOR-swizzled within each half row), and the codes
-// are staged row-major before 16-byte stores.
+// copies (16-byte chunks XOR-swizzled within each half row; 64 rows at a
+// time with the rotation), and the codes are staged row-major before
+// 16-byte stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,9 +47,13 @@ __device__ __forceinline__ void q_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 template <int D, bool ROT>
 __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
   constexpr int E = D / 2;  // elements per thread (half a row)
-  constexpr bool STAGE = D <= 128;  // LDS holds the 128 fp32 rows
+  constexpr bool STAGE = D <= 128;  // rows staged through LDS, 64 at a time
   constexpr int RB = D * 4, CPR = RB / 16, HC = CPR / 2;  // row bytes, chunks per row, per half
-  __shared__ __attribute__((aligned(1024))) char tile[STAGE ? kBlockRows * RB : 16];
+  // rows per staging pass: two passes of 64 rows with the rotation (32 KiB
+  // at d = 128, so that more workgroups share a CU while they transform),
+  // one pass of 128 without (measured: each is the faster choice there)
+  constexpr int NPASS = ROT ? 2 : 1, SR = kBlockRows / NPASS;
+  __shared__ __attribute__((aligned(1024))) char tile[STAGE ? SR * RB : 16];
   const int t = threadIdx.x, r = t >> 1, hf = t & 1;
   const int bh = blockIdx.x / p.nblk, blk = blockIdx.x % p.nblk;
   const int row = blk * kBlockRows + r;
@@ -71,21 +76,30 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
         ub, 0, (int)__builtin_amdgcn_readfirstlane((uint32_t)(rows_left * RB)), 0x00020000);
     const int w = t >> 6, lane = t & 63;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)tile;
-    constexpr int NI = kBlockRows * CPR / 256;  // copies per thread
+    constexpr int NI = SR * CPR / 256;  // copies per thread and pass
+    // with two passes, waves 0-1 take their rows from the first and waves
+    // 2-3 from the second
 #pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      const int sl = (u * 4 + w) * 64 + lane, rr = sl / CPR, pos = sl % CPR;
-      q_dma16(rs, (uint32_t)(rr * RB + ((pos ^ (rr % HC)) << 4)), lds0 + (u * 4 + w) * 1024);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    for (int ps = 0; ps < NPASS; ++ps) {
+      if (ps == 1) __syncthreads();  // the first pass's rows have been read
 #pragma unroll
-    for (int k = 0; k < HC; ++k) {
-      const float4 v = *(const float4*)(tile + r * RB + ((hf * HC + (k ^ (r % HC))) << 4));
-      x[4 * k] = v.x;
-      x[4 * k + 1] = v.y;
-      x[4 * k + 2] = v.z;
-      x[4 * k + 3] = v.w;
+      for (int u = 0; u < NI; ++u) {
+        const int sl = (u * 4 + w) * 64 + lane, rr = sl / CPR, pos = sl % CPR;
+        q_dma16(rs, (uint32_t)((ps * SR + rr) * RB + ((pos ^ (rr % HC)) << 4)), lds0 + (u * 4 + w) * 1024);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (r / SR == ps) {
+        const int lr = r - ps * SR;
+#pragma unroll
+        for (int k = 0; k < HC; ++k) {
+          const float4 v = *(const float4*)(tile + lr * RB + ((hf * HC + (k ^ (lr % HC))) << 4));
+          x[4 * k] = v.x;
+          x[4 * k + 1] = v.y;
+          x[4 * k + 2] = v.z;
+          x[4 * k + 3] = v.w;
+        }
+      }
     }
   } else if (valid) {
     const float4* src = (const float4*)(p.x + base);
