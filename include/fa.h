@@ -70,6 +70,22 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * fa_fwd_gqa — fa_fwd with K and V shared by groups of query heads
+ * (multi-query and grouped-query attention; "FlashAttention (HI)", section on
+ * development and further research, where FlashAttention-2 extends to
+ * multi-query architectures).
+ *   q, o    : [B,H,N,d];  k, v : [B,Hkv,N,d];  lse : [B,H,N] fp32.
+ *   Hkv     : number of K/V heads, 1 <= Hkv <= H with H % Hkv == 0 (else
+ *             FA_ERR_SHAPE).  Query head h of batch b attends with K/V head
+ *             h / (H / Hkv) of batch b: consecutive query heads share one
+ *             K/V head (Hkv = 1: one K/V head for all; Hkv = H: fa_fwd).
+ * Every other argument, the results and the errors are those of fa_fwd.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, int causal, float scale, int dtype,
+               void* stream);
+
+/*
  * fa_fwd_fp8 — the same pass with OCP e4m3fn (finite-only, max 448) inputs,
  * the 8-bit path of "FlashAttention-3 (BN)" / "(FA)" (sections on new
  * hardware capabilities and on low precision).

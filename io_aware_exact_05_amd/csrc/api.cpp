@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiMajor = 1, kAbiMinor = 0;
+constexpr int kAbiMajor = 1, kAbiMinor = 1;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -71,20 +71,21 @@ const char* fa_status_string(int status) {
   return "unknown fa_status";
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-           int d, int causal, float scale, int dtype, void* stream) {
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Hkv, int N, int d, int causal, float scale, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   const int sc = check_shape(B, H, N, d);
   if (sc != FA_OK) return sc;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (!std::isfinite(scale)) return FA_ERR_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_ALIGN;
-  const uint64_t rows = (uint64_t)B * H * N;
-  const uint64_t tbytes = rows * (uint64_t)d * elem_bytes(dtype);
-  const Range rq = range_of(q, tbytes), rk = range_of(k, tbytes), rv = range_of(v, tbytes);
-  const Range ro = range_of(o, tbytes), rl = range_of(lse, rows * 4);
+  const uint64_t rows = (uint64_t)B * H * N, kv_rows = (uint64_t)B * Hkv * N;
+  const uint64_t eb = (uint64_t)d * elem_bytes(dtype);
+  const Range rq = range_of(q, rows * eb), rk = range_of(k, kv_rows * eb), rv = range_of(v, kv_rows * eb);
+  const Range ro = range_of(o, rows * eb), rl = range_of(lse, rows * 4);
   if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) ||
       overlap(rl, rk) || overlap(rl, rv) || overlap(ro, rl))
     return FA_ERR_ALIAS;
@@ -97,12 +98,19 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   p.lse = lse;
   p.BH = B * H;
   p.N = N;
+  p.H = H;
+  p.Hkv = Hkv;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   hipError_t e = (dtype == FA_F32) ? fa::launch_fwd_f32(p, d, causal, s)
                                    : fa::launch_fwd_half(p, d, causal, dtype == FA_BF16, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int causal, float scale, int dtype, void* stream) {
+  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
 }
 
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale,

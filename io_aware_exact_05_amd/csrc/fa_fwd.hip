@@ -136,8 +136,9 @@ void fwd_mfma16(FwdParams p) {
 
   const size_t head = (size_t)bh * N * D;
   const T* __restrict__ qh = (const T*)p.q + head;
-  const T* __restrict__ kh = (const T*)p.k + head;
-  const T* __restrict__ vh = (const T*)p.v + head;
+  const size_t kvhead = (size_t)kv_head(p, bh) * N * D;  // K/V head shared by a group of query heads
+  const T* __restrict__ kh = (const T*)p.k + kvhead;
+  const T* __restrict__ vh = (const T*)p.v + kvhead;
 
   const int qrow0 = qt * BR + w * 32;  // first query row of this wave
   const int myq = qrow0 + ql;          // this lane's query

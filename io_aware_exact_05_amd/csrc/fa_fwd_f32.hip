@@ -45,8 +45,9 @@ __global__ __launch_bounds__(64) void fwd_f32(FwdParams p) {
   const int qt = blockIdx.x / p.BH;
   const size_t head = (size_t)bh * N * D;
   const float* __restrict__ qh = (const float*)p.q + head;
-  const float* __restrict__ kh = (const float*)p.k + head;
-  const float* __restrict__ vh = (const float*)p.v + head;
+  const size_t kvhead = (size_t)kv_head(p, bh) * N * D;  // K/V head shared by a group of query heads
+  const float* __restrict__ kh = (const float*)p.k + kvhead;
+  const float* __restrict__ vh = (const float*)p.v + kvhead;
   const int q0 = qt * BR, myq = q0 + ql;
 
   for (int e = lane; e < BR * D; e += 64) {

@@ -126,8 +126,9 @@ void fwd_wide(FwdParams p) {
 
   const size_t head = (size_t)bh * N * D;
   const T* __restrict__ qh = (const T*)p.q + head;
-  const T* __restrict__ kh = (const T*)p.k + head;
-  const T* __restrict__ vh = (const T*)p.v + head;
+  const size_t kvhead = (size_t)kv_head(p, bh) * N * D;  // K/V head shared by a group of query heads
+  const T* __restrict__ kh = (const T*)p.k + kvhead;
+  const T* __restrict__ vh = (const T*)p.v + kvhead;
 
   const int qrow0 = qt * BR + w * WR;  // first query row of this wave
   // Q operands (B of S^T = K Q^T): block qb, lane holds

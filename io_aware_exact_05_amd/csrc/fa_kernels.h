@@ -16,7 +16,14 @@ struct FwdParams {
   int N;             // sequence length
   int nq;            // query tiles per head (set by the launcher)
   float scale_log2;  // scale * log2(e): scores go straight into exp2
+  int H;             // query heads per batch entry
+  int Hkv;           // K/V heads per batch entry (divides H)
 };
+
+// K/V head of the flattened query head bh = b H + h: b Hkv + h / (H / Hkv).
+__host__ __device__ inline int kv_head(const FwdParams& p, int bh) {
+  return (bh / p.H) * p.Hkv + (bh % p.H) / (p.H / p.Hkv);
+}
 
 // Arguments of the fp8 forward: q8/k8/v8 e4m3fn [B*H, N, d], per-128-row
 // fp32 descales [B*H, nblk], o bf16 [B*H, N, d], lse fp32 [B*H, N].

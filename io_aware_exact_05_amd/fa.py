@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_D
                 -7: "FA_ERR_ALIAS", -8: "FA_ERR_LAUNCH"}
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_quantize_e4m3", "fa_status_string", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_fp8", "fa_quantize_e4m3", "fa_status_string",
+           "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -44,6 +45,8 @@ def _load():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_gqa.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_quantize_e4m3.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp]
@@ -89,29 +92,48 @@ def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: 
                            int(d), int(causal), float(scale), int(dtype), stream))
 
 
+def fa_fwd_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+                   Hkv: int, N: int, d: int, causal: int, scale: float, dtype: int,
+                   stream: int = 0) -> int:
+    """Direct call of fa_fwd_gqa with integer pointers; returns the status."""
+    return int(_lib.fa_fwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, int(B), int(H), int(Hkv),
+                               int(N), int(d), int(causal), float(scale), int(dtype), stream))
+
+
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
            lse: torch.Tensor, causal: bool, scale: float, stream=None) -> None:
-    """fa_fwd on caller-owned device tensors q, k, v, o [B,H,N,d] and lse [B,H,N] fp32."""
+    """Forward pass on caller-owned device tensors: q, o [B,H,N,d], k, v [B,Hkv,N,d] with
+    Hkv dividing H (Hkv = H: fa_fwd; fewer: fa_fwd_gqa), lse [B,H,N] fp32."""
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or o.shape != q.shape:
-        raise ValueError("q, k, v, o must share one [B, H, N, d] shape")
+    if q.dim() != 4 or o.shape != q.shape or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, o must be [B, H, N, d] and k, v one [B, Hkv, N, d] shape")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or tuple(k.shape[2:]) != (N, d) or Hkv < 1 or H % Hkv != 0:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing H")
     if q.dtype not in DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
         raise ValueError("q, k, v, o must share one dtype among float32, float16, bfloat16")
-    B, H, N, d = q.shape
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
         raise ValueError("lse must be float32 of shape [B, H, N]")
-    _check(fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                      B, H, N, d, int(bool(causal)), scale, DTYPE_CODE[q.dtype],
-                      _stream_handle(stream)))
+    if Hkv == H:
+        status = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, H, N, d, int(bool(causal)), scale, DTYPE_CODE[q.dtype],
+                            _stream_handle(stream))
+    else:
+        status = fa_fwd_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), scale,
+                                DTYPE_CODE[q.dtype], _stream_handle(stream))
+    _check(status)
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
               scale: float | None = None, stream=None):
-    """Allocate o and lse with torch and run fa_fwd.  Returns (o, lse)."""
+    """Allocate o and lse with torch and run the forward pass (k, v may have fewer heads than
+    q, their count dividing H).  Returns (o, lse)."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     o = torch.empty_like(q)

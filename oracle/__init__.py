@@ -3,5 +3,6 @@
 Importable only from the tests, the smoke check and the benchmark's CPU
 baseline.  The GPU library must never depend on it.
 """
-from .oracle import attention, attention_rows, build, load, num_threads  # noqa: F401
+from .oracle import (attention, attention_gqa, attention_rows, build, gqa_kv_index, load,  # noqa: F401
+                     num_threads)
 from . import quant_oracle  # noqa: F401

@@ -107,5 +107,28 @@ def attention_rows(q, k, v, causal: bool, scale: float, rows, lib=None):
     return o, lse
 
 
+def gqa_kv_index(H: int, Hkv: int) -> np.ndarray:
+    """K/V head used by each of the H query heads when Hkv K/V heads are shared:
+    consecutive query heads form a group of H / Hkv that shares one K/V head
+    (multi-query attention for Hkv = 1, "FlashAttention (HI)", section on
+    development and further research; grouping consecutive heads is the
+    plain generalisation)."""
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError("Hkv must divide H")
+    return np.arange(H) // (H // Hkv)
+
+
+def attention_gqa(q, k, v, causal: bool, scale: float, lib=None):
+    """Grouped K/V heads: q [B, H, N, d], k and v [B, Hkv, N, d].  Each query head
+    attends with the K/V head gqa_kv_index gives it; the rest is `attention`."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or k.shape[0] != q.shape[0] \
+            or k.shape[2:] != q.shape[2:]:
+        raise ValueError("q must be [B, H, N, d] and k, v one [B, Hkv, N, d] shape")
+    idx = gqa_kv_index(q.shape[1], k.shape[1])
+    return attention(q, np.ascontiguousarray(k[:, idx]), np.ascontiguousarray(v[:, idx]),
+                     causal, scale, lib)
+
+
 def num_threads(lib=None) -> int:
     return int((lib or load()).oracle_num_threads())

@@ -70,6 +70,36 @@ def test_invalid_arguments(kw, code):
     assert _call(**kw) == code
 
 
+# fa_fwd_gqa: k and v hold Hkv heads, Hkv dividing H; everything else as fa_fwd.
+GQ_ARGS = dict(q_ptr=Q, k_ptr=K, v_ptr=V, o_ptr=O, lse_ptr=L, B=B, H=6, Hkv=2, N=N, d=D,
+               causal=0, scale=0.088, dtype=fa.FA_BF16)
+
+
+def _gcall(**kw):
+    a = dict(GQ_ARGS)
+    a.update(kw)
+    return fa.fa_fwd_gqa_raw(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hkv=0), -2), (dict(Hkv=-2), -2), (dict(Hkv=4), -2), (dict(Hkv=7), -2), (dict(Hkv=12), -2),
+    (dict(H=0), -2), (dict(k_ptr=0), -1), (dict(dtype=fa.FA_E4M3), -3), (dict(d=96), -4),
+    (dict(k_ptr=K + 8), -5), (dict(causal=3), -6), (dict(scale=float("nan")), -6),
+    # K and V span B * Hkv * N rows: an output placed just past them is legal,
+    # one inside them is not
+    (dict(o_ptr=K + B * 2 * N * D * 2 - 32), -7), (dict(lse_ptr=V + 16), -7),
+])
+def test_gqa_invalid_arguments(kw, code):
+    assert _gcall(**kw) == code
+
+
+def test_gqa_bounds_use_kv_heads():
+    # with Hkv = 2 of H = 6, K spans a third of Q's bytes: o right after it
+    # passes validation (the launch then fails without a GPU, never FA_ERR_ALIAS)
+    rc = _gcall(o_ptr=K + B * 2 * N * D * 2)
+    assert rc != -7
+
+
 def test_inputs_may_alias_each_other():
     # q, k and v are read-only: sharing one buffer is legal (self-attention on
     # one tensor).  Validation must not reject it; with no GPU the launch
