@@ -28,6 +28,8 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -84,6 +86,56 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int Hkv, int N, int d, int causal, float scale, int dtype,
                void* stream);
+
+/*
+ * fa_bwd — backward pass of fa_fwd: the gradients of L = sum(dout * O) with
+ * respect to q, k and v.  The pages print only the forward formula (section
+ * on the problems of standard attention) and report training speed-ups on
+ * "FlashAttention (HI)" (section on FlashAttention-2) that need its
+ * gradient; differentiating O = softmax(S) V, S = scale Q K^T gives, per
+ * (b, h), with P recomputed from lse (P_ij = exp(S_ij - lse_i), zero for
+ * hidden keys) and D_i = dout_i . O_i:
+ *     dV = P^T dout,  dS = P o (dout V^T - D),  dQ = scale dS K,
+ *     dK = scale dS^T Q.
+ *   q, k, v      : the forward's inputs [B,H,N,d], dtype FA_F16 or FA_BF16
+ *                  (FA_F32 and FA_E4M3 return FA_ERR_DTYPE).
+ *   o, lse       : the forward's outputs for these inputs, causal and scale
+ *                  (o [B,H,N,d] of dtype, lse [B,H,N] fp32).
+ *   dout         : upstream gradient dL/dO [B,H,N,d] of dtype.
+ *   dq, dk, dv   : outputs [B,H,N,d] of dtype, rounded to nearest-even from
+ *                  fp32 accumulators.  P and dS enter the second products
+ *                  rounded to dtype.
+ *   workspace    : device buffer of at least fa_bwd_workspace_bytes(B,H,N)
+ *                  bytes, 16-byte aligned (else FA_ERR_ARG / FA_ERR_ALIGN),
+ *                  owned by the caller; overwritten with per-row statistics
+ *                  (base-2 logsumexp, D).  Its contents between calls carry
+ *                  no meaning.
+ *   causal, scale, d : as in fa_fwd.
+ * Two kernels run in order on `stream`; no atomics, so results are the same
+ * run to run.  Outputs must not overlap the inputs, each other or the
+ * workspace (FA_ERR_ALIAS).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
+           int dtype, void* stream);
+
+/*
+ * fa_bwd_gqa — fa_bwd with K/V heads shared as in fa_fwd_gqa: k, v, dk, dv are
+ * [B,Hkv,N,d]; q, o, dout, dq are [B,H,N,d].  A shared K/V head's gradients
+ * are the sums over the H / Hkv query heads of its group (accumulated in
+ * registers, in a fixed order).  Other arguments as fa_bwd.
+ */
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int H, int Hkv, int N, int d, int causal,
+               float scale, int dtype, void* stream);
+
+/*
+ * Bytes of workspace fa_bwd needs: 8 * B * H * (N rounded up to 128), or 0
+ * when B, H or N < 1.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*
  * fa_fwd_fp8 — the same pass with OCP e4m3fn (finite-only, max 448) inputs,

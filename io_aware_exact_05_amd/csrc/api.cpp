@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiMajor = 1, kAbiMinor = 1;
+constexpr int kAbiMajor = 1, kAbiMinor = 2;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -49,6 +49,9 @@ int check_shape(int B, int H, int N, int d) {
   if (tiles > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
   return FA_OK;
 }
+
+// Rows per head of the backward workspace: N rounded up to 128.
+uint64_t bwd_npad(int N) { return ((uint64_t)N + 127) / 128 * 128; }
 
 }  // namespace
 
@@ -111,6 +114,76 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, int causal, float scale, int dtype, void* stream) {
   return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return (size_t)(2 * 4 * (uint64_t)B * (uint64_t)H * bwd_npad(N));
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int H, int Hkv, int N, int d, int causal, float scale,
+               int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  const int sc = check_shape(B, H, N, d);
+  if (sc != FA_OK) return sc;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_SHAPE;
+  const uint64_t npad = bwd_npad(N);
+  if ((uint64_t)B * H * npad > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N)) return FA_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
+  const uint64_t rows = (uint64_t)B * H * N, kv_rows = (uint64_t)B * Hkv * N;
+  const uint64_t eb = (uint64_t)d * 2;
+  const Range in[6] = {range_of(q, rows * eb),  range_of(k, kv_rows * eb),
+                       range_of(v, kv_rows * eb), range_of(o, rows * eb),
+                       range_of(dout, rows * eb), range_of(lse, rows * 4)};
+  const Range out[4] = {range_of(dq, rows * eb), range_of(dk, kv_rows * eb),
+                        range_of(dv, kv_rows * eb),
+                        range_of(workspace, fa_bwd_workspace_bytes(B, H, N))};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out[j])) return FA_ERR_ALIAS;
+  }
+
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.ws_lse2 = static_cast<float*>(workspace);
+  p.ws_delta = p.ws_lse2 + (uint64_t)B * H * npad;
+  p.BH = B * H;
+  p.N = N;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Npad = (int)npad;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  (void)hipGetLastError();
+  const hipError_t e = fa::launch_bwd_half(p, d, causal, dtype == FA_BF16,
+                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+           int B, int H, int N, int d, int causal, float scale, int dtype, void* stream) {
+  return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d,
+                    causal, scale, dtype, stream);
 }
 
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale,

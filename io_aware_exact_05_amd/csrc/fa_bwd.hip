@@ -1,0 +1,431 @@
+// Attention backward pass for gfx950 (MI355X), fp16/bf16 inputs.
+//
+// The pages print the forward formula only ("FlashAttention (HI)" / "(TL)",
+// section on the problems of standard attention) and report training
+// speed-ups that need its gradient.  Differentiating O = softmax(S) V,
+// S = scale Q K^T, for an upstream gradient dO gives, per (batch, head) and
+// with P recomputed from the forward's logsumexp (P_ij = exp(S_ij - lse_i),
+// zero for hidden keys):
+//     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = dO_i . O_i,
+//     dQ = scale dS K,  dK = scale dS^T Q.
+// As in the forward, no N x N matrix reaches HBM: scores are recomputed tile
+// by tile on chip ("FlashAttention (HI)", tiling section: inputs split into
+// tiles that fit on-chip memory and streamed through it).
+//
+// Two kernels, launched in this order on one stream; neither uses atomics,
+// so results are the same run to run:
+//   bwd_dq    one workgroup per 128 query rows of a head (32 rows per wave).
+//             Q and dO rows sit in registers as MFMA B operands; K and V
+//             tiles stream through an LDS ring (global_load_lds_dwordx4).
+//             Per tile: S^T = K Q^T and dP^T = V dO^T (one query per lane,
+//             like the forward), dS^T in registers, dQ^T += K^T dS^T with K
+//             read transposed from LDS.  Its prologue computes D_i from O
+//             and dO and writes D and the base-2 logsumexp into the
+//             workspace for the second kernel.
+//   bwd_dkdv  one workgroup per 128 keys of a K/V head (32 keys per wave),
+//             looping over every query head that shares that K/V head, so
+//             a shared head's gradients are summed in registers.  K and V
+//             rows sit in registers; Q, dO and the row statistics stream
+//             through LDS.  Per tile: S = Q K^T and dP = dO V^T (one key per
+//             lane), dV^T += dO^T P and dK^T += Q^T dS with Q and dO read
+//             transposed from LDS.
+// The MFMA is v_mfma_f32_32x32x16_{bf16,f16}; P and dS are rounded to the
+// input type for the second products, accumulation is fp32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+constexpr int kBwdNW = 4;  // waves per workgroup (32 rows or keys each)
+
+// BC: key rows per bwd_dq tile; BQ: query rows per bwd_dkdv tile; OCC: waves
+// per SIMD the register budget of each kernel is cut to.
+template <int D> struct BwdCfg;
+template <> struct BwdCfg<64> {
+  static constexpr int BC = 64, BQ = 64, OCC_DQ = 2, OCC_KV = 2;
+};
+template <> struct BwdCfg<128> {
+  static constexpr int BC = 64, BQ = 64, OCC_DQ = 2, OCC_KV = 1;
+};
+template <> struct BwdCfg<256> {
+  static constexpr int BC = 32, BQ = 32, OCC_DQ = 1, OCC_KV = 1;
+};
+constexpr int kBwdST = 2;  // LDS ring stages (prefetch one tile ahead)
+
+// Per-lane LDS read geometry for tiles of 32-row blocks with D columns,
+// unpadded, 16-byte chunks XOR-swizzled by chunk_swz<D>.
+template <int D> struct Geom {
+  int roff, ry;            // row operand: row swap_bits23(lane%32), chunk (2s+g)^swz
+  int toff[2], tx[2];      // transposed operand (ds_read_b64_tr_b16)
+  __device__ __forceinline__ explicit Geom(int lane) {
+    const int ql = lane & 31, g = lane >> 5;
+    const int r = swap_bits23(ql);
+    roff = r * 2 * D;
+    ry = g ^ chunk_swz<D>(r);
+    // In each 16-lane group, lane i addresses row i/4 and columns 4 (i%4) of a
+    // 4 x 16 block; the hardware hands lane i the 4 values of column i.  Rows
+    // 8 g + 4 t + 0..3 of a 16-row half block, columns 32 b + lane % 32.
+    const int trow = (lane & 15) >> 2;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int rr = 8 * g + 4 * t + trow;
+      toff[t] = rr * 2 * D + 8 * (lane & 1);
+      tx[t] = (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ chunk_swz<D>(rr);
+    }
+  }
+};
+
+// C[32 x 32] = A B^T over D: A = 32 rows of an LDS tile block (row i of the
+// MFMA reads tile row swap_bits23(i)), B = 32 rows held in registers (lane
+// l: row l%32, columns 16 s + 8 g .. +8).  Register r of half-wave g of the
+// result is tile row 16 (r/8) + 8 g + r%8, column l%32.
+template <typename T, int D>
+__device__ __forceinline__ f32x16 mm_rows(const char* blk, const Geom<D>& G,
+                                          const i32x4 (&b)[D / 16]) {
+  f32x16 c;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c[r] = 0.f;
+  i32x4 a[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) a[s] = *(const i32x4*)(blk + G.roff + (((2 * s) ^ G.ry) << 4));
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) c = Half<T>::mfma(a[s], b[s], c);
+  return c;
+}
+
+// acc[b] += A_b X over the 32 rows of an LDS tile block: A_b = columns
+// 32 b .. +32 of the block, transposed (MFMA row = tile column); X = the
+// 32 x 32 result of mm_rows (its row index runs over the block's rows),
+// rounded to T.  Register r of the result is column 32 b + 8 (r/4) + 4 g +
+// r%4 of the tile, lane l%32 is X's column.
+template <typename T, int D>
+__device__ __forceinline__ void mm_tr(const char* blk, const Geom<D>& G, const f32x16& x,
+                                      f32x16 (&acc)[D / 32]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    i32x4 xop;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xop[e] = (int)Half<T>::pack2(x[8 * h + 2 * e], x[8 * h + 2 * e + 1]);
+    const char* hb = blk + 16 * h * 2 * D;
+    i16x4 lo[D / 32], hi[D / 32];
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+      lo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(hb + G.toff[0] + (((4 * b) ^ G.tx[0]) << 4)));
+      hi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(hb + G.toff[1] + (((4 * b) ^ G.tx[1]) << 4)));
+    }
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+      const i16x8 a8 = {lo[b][0], lo[b][1], lo[b][2], lo[b][3], hi[b][0], hi[b][1], hi[b][2], hi[b][3]};
+      acc[b] = Half<T>::mfma(__builtin_bit_cast(i32x4, a8), xop, acc[b]);
+    }
+  }
+}
+
+// Store a D-column row from accumulators laid out as mm_tr leaves them
+// (lane = row, register r of block b = column 32 b + 8 (r/4) + 4 g + r%4),
+// times f.
+template <typename T, int D>
+__device__ __forceinline__ void store_row(T* row, const f32x16 (&acc)[D / 32], float f, int g) {
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      uint2 v;
+      v.x = Half<T>::pack2(acc[b][4 * a] * f, acc[b][4 * a + 1] * f);
+      v.y = Half<T>::pack2(acc[b][4 * a + 2] * f, acc[b][4 * a + 3] * f);
+      *(uint2*)(row + 32 * b + 8 * a + 4 * g) = v;
+    }
+}
+
+__device__ __forceinline__ float lo16(int x, bool bf) {
+  const unsigned short h = (unsigned short)(x & 0xffff);
+  return bf ? __builtin_bit_cast(float, (unsigned)h << 16) : (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ float hi16(int x, bool bf) {
+  const unsigned short h = (unsigned short)((unsigned)x >> 16);
+  return bf ? __builtin_bit_cast(float, (unsigned)h << 16) : (float)__builtin_bit_cast(_Float16, h);
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and the row statistics for bwd_dkdv)
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kBwdNW) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::OCC_DQ, BwdCfg<D>::OCC_DQ)))
+void bwd_dq(BwdParams p) {
+  constexpr int NW = kBwdNW, BR = 32 * NW, BC = BwdCfg<D>::BC, ST = kBwdST;
+  constexpr int RB = 2 * D, TB = BC * RB, CPR = D / 8, CPT = BC * CPR / (64 * NW);
+  constexpr int NS = D / 16, NKB = BC / 32, ND = D / 32;
+  constexpr bool BF = __is_same(T, __bf16);
+  static_assert(BC * CPR % (64 * NW) == 0, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * 2 * TB];  // [stage][K, V]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  int bh, qt;
+  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt);
+  const size_t head = (size_t)bh * N * D;
+  const size_t kvhead = (size_t)kv_head_of(p.H, p.Hkv, bh) * N * D;
+  const T* __restrict__ kh = (const T*)p.k + kvhead;
+  const T* __restrict__ vh = (const T*)p.v + kvhead;
+
+  const int qrow0 = qt * BR + w * 32;
+  const int myq = qrow0 + ql;
+  const int rq = min(myq, N - 1);
+
+  // B operands: Q and dO rows of this lane's query; D_i = dO_i . O_i from
+  // this lane's half of the columns plus the other half-wave's.
+  i32x4 qop[NS], dop[NS];
+  float dl = 0.f;
+  {
+    const size_t ro = head + (size_t)rq * D + 8 * g;
+    const T* qr = (const T*)p.q + ro;
+    const T* dr = (const T*)p.dout + ro;
+    const T* orow = (const T*)p.o + ro;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qop[s] = *(const i32x4*)(qr + 16 * s);
+      dop[s] = *(const i32x4*)(dr + 16 * s);
+      const i32x4 ov = *(const i32x4*)(orow + 16 * s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dl += lo16(dop[s][e], BF) * lo16(ov[e], BF) + hi16(dop[s][e], BF) * hi16(ov[e], BF);
+    }
+  }
+  dl = pair_sum(dl);
+  const float lse2 = p.lse[(size_t)bh * N + rq] * 1.44269504088896340736f;  // log2(e)
+  if (g == 0) {  // rows N .. Npad-1: P = 2^-inf = 0 and D = 0 in bwd_dkdv
+    p.ws_lse2[(size_t)bh * p.Npad + myq] = myq < N ? lse2 : __builtin_huge_valf();
+    p.ws_delta[(size_t)bh * p.Npad + myq] = myq < N ? dl : 0.f;
+  }
+  // Drain this wave's own loads and stores: the tile copies below are counted
+  // on the same vmcnt and the waits in the loop count only those.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
+  const int nt = (kv_end + BC - 1) / BC;
+  const int jlast = qrow0 >= N ? -1 : CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1;
+
+  int ld_off[CPT], ld_row[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int s = (u * NW + w) * 64 + lane, row = s / CPR, c = s % CPR;
+    ld_row[u] = row;
+    ld_off[u] = (c ^ chunk_swz<D>(row)) * 8;
+  }
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+  auto issue_tile = [&](int j, int stage) __attribute__((always_inline)) {
+    const uint32_t dst = smem_base + stage * 2 * TB;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const size_t row = (size_t)min(j * BC + ld_row[u], N - 1);
+      const uint32_t lo = dst + (u * NW + w) * 1024;
+      dma16(kh + row * D + ld_off[u], lo);
+      dma16(vh + row * D + ld_off[u], lo + TB);
+    }
+  };
+
+  const Geom<D> G(lane);
+  f32x16 acc[ND];
+#pragma unroll
+  for (int b = 0; b < ND; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+  const float c = p.scale_log2;
+
+  issue_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < nt; ++j) {
+    if (j + 1 < nt) issue_tile(j + 1, (j + 1) % ST);
+    if (j <= jlast) {
+      const char* sk = smem + (j % ST) * 2 * TB;
+      const char* sv = sk + TB;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        f32x16 s = mm_rows<T, D>(sk + kb * 32 * RB, G, qop);
+        const f32x16 dp = mm_rows<T, D>(sv + kb * 32 * RB, G, dop);
+        // register r holds key key0 + 16 (r/8) + r%8
+        const int key0 = j * BC + kb * 32 + 8 * g;
+        const bool need_mask = (j * BC + kb * 32 + 32 > N) || (CAUSAL && j * BC + kb * 32 + 31 > qrow0);
+        const int rel = (CAUSAL ? min(myq, N - 1) : N - 1) - key0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+          if (need_mask) pr = (16 * (r >> 3) + (r & 7) <= rel) ? pr : 0.f;
+          s[r] = pr * (dp[r] - dl);
+        }
+        mm_tr<T, D>(sk + kb * 32 * RB, G, s, acc);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (myq < N) store_row<T, D>((T*)p.dq + head + (size_t)myq * D, acc, p.scale, g);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kBwdNW) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::OCC_KV, BwdCfg<D>::OCC_KV)))
+void bwd_dkdv(BwdParams p) {
+  constexpr int NW = kBwdNW, BK = 32 * NW, BQ = BwdCfg<D>::BQ, ST = kBwdST;
+  constexpr int RB = 2 * D, TB = BQ * RB, CPR = D / 8, CPT = BQ * CPR / (64 * NW);
+  constexpr int NS = D / 16, NQB = BQ / 32, ND = D / 32;
+  constexpr int SB = 2 * BQ * 4;          // row statistics per tile: base-2 lse, then D
+  constexpr int STB = 2 * TB + SB;        // bytes per stage: Q, dO, statistics
+  constexpr int SL = SB / 16 / NW;        // statistics chunks per wave
+  static_assert(BQ * CPR % (64 * NW) == 0 && SB % (16 * NW) == 0 && SL <= 64, "tile split");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * STB];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  const int BHkv = p.BH / (p.H / p.Hkv), grp = p.H / p.Hkv;
+  int kvbh, t;
+  decode_block(blockIdx.x, BHkv, p.nq, CAUSAL, kvbh, t);
+  const int kblk = CAUSAL ? p.nq - 1 - t : t;  // causal: low key blocks (most work) first
+  const int b = kvbh / p.Hkv, gk = kvbh % p.Hkv;
+  const int qh0 = b * p.H + gk * grp;          // first query head of the group
+  const size_t kvhead = (size_t)kvbh * N * D;
+
+  const int k0 = kblk * BK + w * 32;
+  const int mykey = k0 + ql;
+  i32x4 kop[NS], vop[NS];
+  {
+    const size_t ro = kvhead + (size_t)min(mykey, N - 1) * D + 8 * g;
+    const T* kr = (const T*)p.k + ro;
+    const T* vr = (const T*)p.v + ro;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kop[s] = *(const i32x4*)(kr + 16 * s);
+      vop[s] = *(const i32x4*)(vr + 16 * s);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qs = CAUSAL ? (kblk * BK) / BQ : 0;  // first query tile that sees a key of the block
+  const int cnt = nqt - qs;
+  const int ntile = grp * cnt;
+
+  int ld_off[CPT], ld_row[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int s = (u * NW + w) * 64 + lane, row = s / CPR, cc = s % CPR;
+    ld_row[u] = row;
+    ld_off[u] = (cc ^ chunk_swz<D>(row)) * 8;
+  }
+  // statistics chunk of this lane (lanes < SL): chunk w SL + lane of
+  // [lse2 (BQ floats), D (BQ floats)]
+  const int sci = w * SL + lane;
+  const int s_arr = sci / (BQ / 4), s_off = (sci % (BQ / 4)) * 4;
+  const float* s_src = (s_arr == 0 ? p.ws_lse2 : p.ws_delta) + s_off;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+  auto issue_tile = [&](int j, int stage) __attribute__((always_inline)) {
+    const int hh = j / cnt, qt = qs + j % cnt;
+    const int bhq = qh0 + hh;
+    const size_t hq = (size_t)bhq * N * D;
+    const T* qsrc = (const T*)p.q + hq;
+    const T* dsrc = (const T*)p.dout + hq;
+    const uint32_t dst = smem_base + stage * STB;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const size_t row = (size_t)min(qt * BQ + ld_row[u], N - 1);
+      const uint32_t lo = dst + (u * NW + w) * 1024;
+      dma16(qsrc + row * D + ld_off[u], lo);
+      dma16(dsrc + row * D + ld_off[u], lo + TB);
+    }
+    if (lane < SL) dma16(s_src + (size_t)bhq * p.Npad + qt * BQ, dst + 2 * TB + w * SL * 16);
+  };
+
+  const Geom<D> G(lane);
+  f32x16 acck[ND], accv[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acck[d][r] = accv[d][r] = 0.f;
+  const float c = p.scale_log2;
+
+  if (ntile > 0) issue_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < ntile; ++j) {
+    if (j + 1 < ntile) issue_tile(j + 1, (j + 1) % ST);
+    const int q0 = (qs + j % cnt) * BQ;
+    if (!CAUSAL || q0 + BQ - 1 >= k0) {  // else every query of the tile precedes every key of the wave
+      const char* sq = smem + (j % ST) * STB;
+      const char* sd = sq + TB;
+      const float* sst = (const float*)(sq + 2 * TB);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        f32x16 s = mm_rows<T, D>(sq + qb * 32 * RB, G, kop);
+        f32x16 dp = mm_rows<T, D>(sd + qb * 32 * RB, G, vop);
+        // register r holds query q0 + 32 qb + 16 (r/8) + 8 g + r%8
+        float l2[16], dd[16];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float4* a = (const float4*)(sst + 32 * qb + 16 * hh + 8 * g);
+          const float4* bq = (const float4*)(sst + BQ + 32 * qb + 16 * hh + 8 * g);
+          const float4 a0 = a[0], a1 = a[1], b0 = bq[0], b1 = bq[1];
+          l2[8 * hh + 0] = a0.x; l2[8 * hh + 1] = a0.y; l2[8 * hh + 2] = a0.z; l2[8 * hh + 3] = a0.w;
+          l2[8 * hh + 4] = a1.x; l2[8 * hh + 5] = a1.y; l2[8 * hh + 6] = a1.z; l2[8 * hh + 7] = a1.w;
+          dd[8 * hh + 0] = b0.x; dd[8 * hh + 1] = b0.y; dd[8 * hh + 2] = b0.z; dd[8 * hh + 3] = b0.w;
+          dd[8 * hh + 4] = b1.x; dd[8 * hh + 5] = b1.y; dd[8 * hh + 6] = b1.z; dd[8 * hh + 7] = b1.w;
+        }
+        const bool need_mask = CAUSAL && q0 + 32 * qb < k0 + 31;
+        const int lo = mykey - (q0 + 32 * qb + 8 * g);  // visible iff 16 (r/8) + r%8 >= lo
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
+          if (need_mask) pr = (16 * (r >> 3) + (r & 7) >= lo) ? pr : 0.f;
+          s[r] = pr;
+          dp[r] = pr * (dp[r] - dd[r]);
+        }
+        mm_tr<T, D>(sd + qb * 32 * RB, G, s, accv);
+        mm_tr<T, D>(sq + qb * 32 * RB, G, dp, acck);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (mykey < N) {
+    store_row<T, D>((T*)p.dk + kvhead + (size_t)mykey * D, acck, p.scale, g);
+    store_row<T, D>((T*)p.dv + kvhead + (size_t)mykey * D, accv, 1.0f, g);
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
+  constexpr int BR = 32 * kBwdNW;
+  BwdParams a = p;
+  a.nq = p.Npad / BR;  // bwd_dq covers every workspace row
+  hipLaunchKernelGGL((bwd_dq<T, D, CAUSAL>), dim3((unsigned)(a.nq * p.BH)), dim3(64 * kBwdNW), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int BHkv = p.BH / (p.H / p.Hkv);
+  BwdParams b = p;
+  b.nq = (p.N + BR - 1) / BR;  // key blocks per K/V head
+  hipLaunchKernelGGL((bwd_dkdv<T, D, CAUSAL>), dim3((unsigned)(b.nq * BHkv)), dim3(64 * kBwdNW), 0, s, b);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_bwd_d(const BwdParams& p, int d, int causal, hipStream_t s) {
+  switch (d) {
+    case 64:  return causal ? launch_bwd_t<T, 64, true>(p, s) : launch_bwd_t<T, 64, false>(p, s);
+    case 128: return causal ? launch_bwd_t<T, 128, true>(p, s) : launch_bwd_t<T, 128, false>(p, s);
+    case 256: return causal ? launch_bwd_t<T, 256, true>(p, s) : launch_bwd_t<T, 256, false>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_half(const BwdParams& p, int d, int causal, int is_bf16, hipStream_t s) {
+  return is_bf16 ? launch_bwd_d<__bf16>(p, d, causal, s) : launch_bwd_d<_Float16>(p, d, causal, s);
+}
+
+}  // namespace fa

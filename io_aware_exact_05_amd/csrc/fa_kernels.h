@@ -25,6 +25,39 @@ __host__ __device__ inline int kv_head(const FwdParams& p, int bh) {
   return (bh / p.H) * p.Hkv + (bh % p.H) / (p.H / p.Hkv);
 }
 
+// K/V head of flattened query head bh when Hkv K/V heads serve H query heads.
+__host__ __device__ inline int kv_head_of(int H, int Hkv, int bh) {
+  return (bh / H) * Hkv + (bh % H) / (H / Hkv);
+}
+
+// Arguments of the backward pass.  q, o, dout, dq: [B*H, N, d]; k, v, dk,
+// dv: [B*Hkv, N, d]; lse fp32 [B*H, N] from the forward.  ws_lse2 and
+// ws_delta are the two halves of the caller's workspace, fp32 [B*H, Npad]
+// each (Npad = N rounded up to 128): bwd_dq writes the base-2 logsumexp and
+// D_i = dO_i . O_i of every row there (rows >= N: +inf and 0), bwd_dkdv
+// reads them.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws_lse2;
+  float* ws_delta;
+  int BH;            // B * H
+  int N;
+  int H;
+  int Hkv;
+  int Npad;
+  int nq;            // tiles per head of the kernel being launched (set by the launcher)
+  float scale;
+  float scale_log2;  // scale * log2(e)
+};
+
 // Arguments of the fp8 forward: q8/k8/v8 e4m3fn [B*H, N, d], per-128-row
 // fp32 descales [B*H, nblk], o bf16 [B*H, N, d], lse fp32 [B*H, N].
 struct Fp8Params {
@@ -68,6 +101,8 @@ int wide_blocks_per_cu(int d, int causal);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, int causal, hipStream_t s);
 // e4m3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4).  d = 128.
 hipError_t launch_fwd_fp8(const Fp8Params& p, int d, int causal, hipStream_t s);
+// Backward pass, fp16 / bf16 (fa_bwd.hip): bwd_dq then bwd_dkdv on stream s.
+hipError_t launch_bwd_half(const BwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
 // fp32 -> e4m3 block quantiser, optional randomised Hadamard rotation.
 hipError_t launch_quantize_e4m3(const QuantParams& p, int d, int rotate, hipStream_t s);
 

@@ -28,8 +28,8 @@ STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_D
                 -7: "FA_ERR_ALIAS", -8: "FA_ERR_LAUNCH"}
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_fp8", "fa_quantize_e4m3", "fa_status_string",
-           "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_bytes", "fa_fwd_fp8",
+           "fa_quantize_e4m3", "fa_status_string", "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -47,6 +47,14 @@ def _load():
     lib.fa_fwd.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_gqa.restype = i
+    sz = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i,
+                               vp]
+    lib.fa_bwd_gqa.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_quantize_e4m3.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp]
@@ -140,6 +148,80 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, causal, scale, stream)
     return o, lse
+
+
+# ----------------------------------------------------------------------------
+# backward pass
+# ----------------------------------------------------------------------------
+
+def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(_lib.fa_bwd_workspace_bytes(int(B), int(H), int(N)))
+
+
+def fa_bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, B, H, N, d, causal, scale, dtype,
+               stream=0) -> int:
+    """Direct call of fa_bwd with integer pointers; returns the status."""
+    return int(_lib.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, int(B), int(H), int(N),
+                           int(d), int(causal), float(scale), int(dtype), stream))
+
+
+def fa_bwd_gqa_raw(q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, B, H, Hkv, N, d, causal, scale,
+                   dtype, stream=0) -> int:
+    """Direct call of fa_bwd_gqa with integer pointers; returns the status."""
+    return int(_lib.fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, int(B), int(H),
+                               int(Hkv), int(N), int(d), int(causal), float(scale), int(dtype),
+                               stream))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
+           stream=None) -> None:
+    """Backward pass on caller-owned device tensors: q, o, dout, dq [B,H,N,d]; k, v, dk, dv
+    [B,Hkv,N,d] (Hkv dividing H); lse [B,H,N] fp32 from the forward; workspace a uint8
+    device tensor of at least bwd_workspace_bytes(B, H, N) bytes."""
+    named = (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse), ("dq", dq),
+             ("dk", dk), ("dv", dv), ("workspace", workspace))
+    for name, t in named:
+        _dev(name, t)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or tuple(k.shape[2:]) != (N, d) or Hkv < 1 or H % Hkv != 0:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing H")
+    for name, t in (("o", o), ("dout", dout), ("dq", dq)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    for name, t in (("v", v), ("dk", dk), ("dv", dv)):
+        if t.shape != k.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match k in shape and q in dtype")
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("the backward pass takes float16 or bfloat16")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be float32 of shape [B, H, N]")
+    wsb = workspace.numel() * workspace.element_size()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), wsb)
+    tail = (d, int(bool(causal)), scale, DTYPE_CODE[q.dtype], _stream_handle(stream))
+    if Hkv == H:
+        status = fa_bwd_raw(*args, B, H, N, *tail)
+    else:
+        status = fa_bwd_gqa_raw(*args, B, H, Hkv, N, *tail)
+    _check(status)
+
+
+def attention_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+                  stream=None):
+    """Allocate dq, dk, dv and the workspace with torch and run the backward pass.
+    Returns (dq, dk, dv)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    B, H, N, _ = q.shape
+    ws = torch.empty(bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------

@@ -122,3 +122,9 @@ def rotation_signs(d: int, seed: int = 0) -> torch.Tensor:
     """The +-1 diagonal of the randomised Hadamard rotation (fp32, CPU)."""
     rng = np.random.default_rng(np.random.SeedSequence([7777, seed, d]))
     return torch.from_numpy(rng.choice(np.array([-1.0, 1.0], np.float32), d))
+
+
+def upstream_grad(shape, dtype: str, seed: int) -> torch.Tensor:
+    """Seeded standard-normal upstream gradient dL/dO of the given shape (CPU, storage dtype)."""
+    rng = np.random.default_rng(np.random.SeedSequence([4242, seed, *shape]))
+    return _round(rng.standard_normal(tuple(shape)), dtype)

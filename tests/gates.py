@@ -56,3 +56,74 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, out_dtype: str, what: str = ""):
                              f"ref={o_ref[idx]!r} ({int(bad.sum())} elements) {stats}")
     assert (lse_err <= LSE_ABS_TOL).all(), f"{what}: LSE gate failed {stats}"
     return stats
+
+
+# ---------------------------------------------------------------------------
+# Backward pass.  The GPU rounds three things the fp64 gradient does not:
+#  - P (relative error <= u) before dV = P^T dO;
+#  - dS (relative <= u) before dQ = scale dS K and dK = scale dS^T Q;
+#  - its own O (the forward's output, whose error is <= u |O| + u (P |V|)
+#    per element: output rounding plus the forward's rounded P), which
+#    enters D_i = dO_i . O_i and through it every dS_ij as P_ij * error(D_i);
+# and then rounds each gradient to the output type (<= u |g|).  With u the
+# unit roundoff of the input type, the elementwise bounds are
+#   |dV err| <= u (P^T |dO|) + u |dV|
+#   |dQ err| <= scale ((u |dS| + P e_D) |K|) + u |dQ|,  e_D = u |dO| . (|O| + P |V|)
+#   |dK err| <= scale ((u |dS| + P e_D)^T |Q|) + u |dK|
+# (shared K/V heads: sums over the group).  fp32 accumulation, exp2 and the
+# forward's logsumexp add errors near 2^-20 relative; the gate is twice the
+# bound plus 1e-5 of the tensor's largest magnitude.
+# ---------------------------------------------------------------------------
+_UNIT = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def bwd_bounds(q, k, v, do, causal, scale, dtype, heads=None):
+    """Elementwise error bounds (fp64 numpy) for dq, dk, dv; heads as in
+    oracle.attention_bwd (K/V heads b*Hkv + g), others left NaN."""
+    u = _UNIT[dtype]
+    q, k, v, do = widen(q), widen(k), widen(v), widen(do)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    grp = H // Hkv
+    bq, bk, bv = (np.full(x.shape, np.nan) for x in (q, k, v))
+    todo = range(B * Hkv) if heads is None else sorted(set(int(x) for x in heads))
+    for flat in todo:
+        b, g = divmod(flat, Hkv)
+        bk[b, g] = 0.0
+        bv[b, g] = 0.0
+        for h in range(g * grp, (g + 1) * grp):
+            s = scale * (q[b, h] @ k[b, g].T)
+            if causal:
+                s = np.where(np.tril(np.ones((N, N), dtype=bool)), s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ v[b, g]
+            dp = do[b, h] @ v[b, g].T
+            ds = p * (dp - (do[b, h] * o).sum(axis=1)[:, None])
+            e_d = u * (np.abs(do[b, h]) * (np.abs(o) + p @ np.abs(v[b, g]))).sum(axis=1)
+            w = u * np.abs(ds) + p * e_d[:, None]
+            dq = scale * (ds @ k[b, g])
+            bq[b, h] = abs(scale) * (w @ np.abs(k[b, g])) + u * np.abs(dq)
+            bk[b, g] += abs(scale) * (w.T @ np.abs(q[b, h])) + u * np.abs(scale * (ds.T @ q[b, h]))
+            bv[b, g] += u * (p.T @ np.abs(do[b, h])) + u * np.abs(p.T @ do[b, h])
+    return bq, bk, bv
+
+
+def check_bwd(grads_gpu, grads_ref, bounds, what=""):
+    """Assert |gpu - ref| <= 2 bound + 1e-5 max|ref| for each of dq, dk, dv over the
+    elements where the reference is defined (not NaN); return the worst error/gate ratios."""
+    ratios = {}
+    for name, g, r, bd in zip(("dq", "dk", "dv"), grads_gpu, grads_ref, bounds):
+        g = widen(g)
+        sel = ~np.isnan(r)
+        assert g.shape == r.shape, (name, g.shape, r.shape)
+        assert np.isfinite(g[sel]).all(), f"{what}: non-finite {name}"
+        err = np.abs(g[sel] - r[sel])
+        gate = 2.0 * bd[sel] + 1e-5 * np.abs(r[sel]).max(initial=0.0)
+        ratio = err / np.maximum(gate, 1e-300)
+        ratios[name] = float(ratio.max(initial=0.0))
+        if (err > gate).any():
+            i = int(np.argmax(err - gate))
+            raise AssertionError(f"{what}: {name} gate failed: gpu={g[sel][i]!r} ref={r[sel][i]!r} "
+                                 f"gate={gate[i]!r} ({int((err > gate).sum())} elements) {ratios}")
+    return ratios

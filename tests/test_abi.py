@@ -154,3 +154,53 @@ def _qz(**kw):
 ])
 def test_quantize_invalid_arguments(kw, code):
     assert _qz(**kw) == code
+
+
+# ----------------------------- backward pass -------------------------------
+# Fake addresses 16 MiB apart (every tensor below is smaller than that).
+BW = dict(zip(("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"),
+              (0x40000000 + i * 0x1000000 for i in range(10))))
+
+
+def _bwd_args(**kw):
+    a = dict(BW, ws_bytes=fa.bwd_workspace_bytes(B, H, N), B=B, H=H, N=N, d=D, causal=1,
+             scale=0.088, dtype=fa.FA_BF16)
+    a.update(kw)
+    return a
+
+
+def _bwd(**kw):
+    return fa.fa_bwd_raw(**_bwd_args(**kw))
+
+
+def test_bwd_workspace_bytes():
+    assert fa.bwd_workspace_bytes(B, H, N) == 8 * B * H * 128
+    assert fa.bwd_workspace_bytes(1, 1, 128) == 8 * 128
+    assert fa.bwd_workspace_bytes(1, 1, 129) == 8 * 256
+    assert fa.bwd_workspace_bytes(0, 1, 1) == 0 and fa.bwd_workspace_bytes(1, 1, 0) == 0
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"])
+def test_bwd_null_pointer(which):
+    assert _bwd(**{which: 0}) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(N=0), -2), (dict(d=96), -4),
+    (dict(dtype=fa.FA_F32), -3), (dict(dtype=fa.FA_E4M3), -3), (dict(dtype=7), -3),
+    (dict(causal=2), -6), (dict(scale=float("nan")), -6), (dict(scale=float("inf")), -6),
+    (dict(ws_bytes=8 * B * H * 128 - 1), -6), (dict(ws_bytes=0), -6),
+    (dict(q=BW["q"] + 8), -5), (dict(dq=BW["dq"] + 2), -5), (dict(lse=BW["lse"] + 2), -5),
+    (dict(ws=BW["ws"] + 4), -5),
+    (dict(dq=BW["q"]), -7), (dict(dk=BW["dout"] + 4096), -7), (dict(dv=BW["dk"]), -7),
+    (dict(ws=BW["lse"]), -7), (dict(dq=BW["ws"]), -7),
+])
+def test_bwd_invalid_arguments(kw, code):
+    assert _bwd(**kw) == code
+
+
+@pytest.mark.parametrize("Hkv,code", [(0, -2), (2, -2), (4, -2), (-1, -2)])
+def test_bwd_gqa_invalid_heads(Hkv, code):
+    a = _bwd_args()
+    a["Hkv"] = Hkv
+    assert fa.fa_bwd_gqa_raw(**a) == code
