@@ -19,6 +19,11 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                                 three block quantisations, Q and K
                                                 rotated, then the fp8 attention;
                                                 the quantiser is reported apart)
+       python bench.py --bwd                   (the backward pass of the same
+                                                workload instead: dQ, dK, dV from
+                                                the forward's O and logsumexp;
+                                                flops 2.5x the forward's: five
+                                                N x N x d products instead of two)
        python bench.py --profile-launches K    (only K non-causal launches; for
                                                 rocprofv3 runs)
        python bench.py --copy-calib            (one 1 GiB device copy: the HBM
@@ -95,6 +100,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="CPU-baseline budget; the sample is sized to about this")
     ap.add_argument("--profile-launches", type=int, default=0)
+    ap.add_argument("--bwd", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     return ap.parse_args()
 
@@ -141,6 +147,19 @@ def main():
         qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
         data.append((w, (q, k, v)))
+        if args.bwd:
+            if w.dtype not in ("bf16", "f16"):
+                sys.exit("the backward pass takes bf16 or f16 workloads")
+            o = torch.empty_like(qd)
+            fa.fa_fwd(qd, kd, vd, o, lse, bool(w.causal), w.scale, stream)
+            do = inputs.upstream_grad((w.B, w.H, w.N, w.d), w.dtype, w.config_id).to(dev)
+            dq_, dk_, dv_ = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+            ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+            name = ("causal" if w.causal else "noncausal") + (f"_d{w.d}" if multi_d else "")
+            parts.append((name, w,
+                          lambda w=w, t=(qd, kd, vd, o, do, lse, dq_, dk_, dv_, ws):
+                          fa.fa_bwd(*t, bool(w.causal), w.scale, stream)))
+            continue
         if not fp8:
             o = torch.empty_like(qd)
             name = ("causal" if w.causal else "noncausal") + (f"_d{w.d}" if multi_d else "")
@@ -192,9 +211,11 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
+    # algorithmic flops of one launch: the forward's 2 products, the backward's 5
+    fmul = 2.5 if args.bwd else 1.0
     ms_step = (t1 - t0) * 1e3 / K
     per_part_ms = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)] for i in range(len(parts))]
-    step_flops = sum(w.flops for w, _ in data)
+    step_flops = sum(w.flops for w, _ in data) * fmul
     value = step_flops / (ms_step * 1e-3) / 1e12
     dtype = cases[0].dtype
     peak = PEAK_TFLOPS[dtype]
@@ -205,7 +226,7 @@ def main():
         rep_i = {"ms_median": round(float(np.median(t)), 5), "ms_min": round(float(t.min()), 5),
                  "ms_p90": round(float(np.percentile(t, 90)), 5)}
         if w is not None:
-            tf = w.flops / (np.median(t) * 1e-3) / 1e12
+            tf = fmul * w.flops / (np.median(t) * 1e-3) / 1e12
             rep_i.update(tflops=round(tf, 2), pct_of_peak=round(100 * tf / peak, 2))
         else:  # quantiser: 4 bytes read and 1 written per element, plus the descales
             w0 = cases[0]
@@ -223,21 +244,24 @@ def main():
            for i, t in enumerate(per_part_ms)]
     dom = int(np.argmax(avg))
     wd = parts[dom][1]
-    achieved = wd.flops / (avg[dom] * 1e-3) / 1e12
-    traffic = measured_traffic() if (wd.config_id, wd.case_id) == (2, 0) else None
-    kname = kernel_name(wd)
+    achieved = fmul * wd.flops / (avg[dom] * 1e-3) / 1e12
+    traffic = measured_traffic() if (wd.config_id, wd.case_id) == (2, 0) and not args.bwd else None
+    kname = "bwd_dq+bwd_dkdv" if args.bwd else kernel_name(wd)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": f"{kname} {wd.label()}", "avg_launch_ms": round(avg[dom], 5)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(data, args.cpu_seconds)
+        cpu = cpu_baseline_bwd(data, args.cpu_seconds) if args.bwd else \
+            cpu_baseline(data, args.cpu_seconds)
 
     label = ", ".join(("causal" if w.causal else "noncausal") for w, _ in data)
     w0 = cases[0]
     out = {
-        "metric": "attention fwd TFLOPS (4*B*H*N^2*d, halved if causal) and % of MFMA peak, 1 GPU",
+        "metric": ("attention bwd TFLOPS (10*B*H*N^2*d, halved if causal) and % of MFMA peak, 1 GPU"
+                   if args.bwd else
+                   "attention fwd TFLOPS (4*B*H*N^2*d, halved if causal) and % of MFMA peak, 1 GPU"),
         "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
@@ -245,7 +269,8 @@ def main():
         "config": {"workload": f"{w0.name} ({label})", "B": w0.B, "H": w0.H, "N": w0.N,
                    "d": w0.d, "causal": [w.causal for w, _ in data], "dtype": dtype,
                    "step_flops": step_flops,
-                   **({"step": "quantise Q, K (rotated), V; fp8 attention"} if fp8 else {})},
+                   **({"step": "quantise Q, K (rotated), V; fp8 attention"} if fp8 else {}),
+                   **({"step": "backward: dQ, dK, dV from O, logsumexp and dO"} if args.bwd else {})},
         "cases": case_rep,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -287,6 +312,43 @@ def cpu_baseline(data, budget_s):
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{take} of {n_heads} heads (all {data[0][0].N} rows each) of every case "
                       f"of the step, fp64, OpenMP over query rows"}
+
+
+def cpu_baseline_bwd(data, budget_s):
+    """fp64 backward oracle on whole heads of the same workload, sized to ~budget_s."""
+    import oracle
+    from io_aware_exact_05_amd import inputs
+
+    t_head = 0.0
+    for w, (q, k, v) in data:
+        do = inputs.upstream_grad((1, 1, w.N, w.d), w.dtype, w.config_id)
+        t = time.perf_counter()
+        oracle.attention_bwd(q[:1, :1], k[:1, :1], v[:1, :1], do, w.causal, w.scale)
+        t_head += time.perf_counter() - t
+    n_heads = data[0][0].B * data[0][0].H
+    take = int(max(1, min(n_heads, budget_s // max(t_head, 1e-6))))
+    flops = 0.0
+    t = time.perf_counter()
+    for w, (q, k, v) in data:
+        do = inputs.upstream_grad((w.B, w.H, w.N, w.d), w.dtype, w.config_id)
+        b_, rem = take // w.H, take % w.H
+        sl = [(slice(0, b_), slice(None))] if b_ else []
+        if rem:
+            sl.append((slice(b_, b_ + 1), slice(0, rem)))
+        for bs, hs in sl:
+            oracle.attention_bwd(q[bs, hs], k[bs, hs], v[bs, hs], do[bs, hs], w.causal, w.scale)
+        flops += 2.5 * w.flops * take / n_heads
+    dt = time.perf_counter() - t
+    try:  # threads of numpy's BLAS, which runs the matrix products
+        from threadpoolctl import threadpool_info
+        threads = max([p["num_threads"] for p in threadpool_info() if p["user_api"] == "blas"],
+                      default=1)
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{take} of {n_heads} heads (all {data[0][0].N} rows each) of every case "
+                      f"of the step, fp64 numpy (BLAS threads for the matrix products)"}
 
 
 if __name__ == "__main__":

@@ -42,18 +42,45 @@ namespace fa {
 constexpr int kBwdNW = 4;  // waves per workgroup (32 rows or keys each)
 
 // BC: key rows per bwd_dq tile; BQ: query rows per bwd_dkdv tile; OCC: waves
-// per SIMD the register budget of each kernel is cut to.
+// per SIMD the register budget of each kernel is cut to; ST_*: LDS ring
+// stages of each kernel (tiles are prefetched ST - 1 ahead).  The FA_BWD_* macros
+// exist for tuning builds only.
+#ifndef FA_BWD_D64_BC
+#define FA_BWD_D64_BC 64
+#endif
+#ifndef FA_BWD_D64_BQ
+#define FA_BWD_D64_BQ 64
+#endif
+#ifndef FA_BWD_D128_BC
+#define FA_BWD_D128_BC 64
+#endif
+#ifndef FA_BWD_D128_BQ
+#define FA_BWD_D128_BQ 64
+#endif
+#ifndef FA_BWD_D64_STDQ
+#define FA_BWD_D64_STDQ 2
+#endif
+#ifndef FA_BWD_D64_STKV
+#define FA_BWD_D64_STKV 2
+#endif
+#ifndef FA_BWD_D128_STDQ
+#define FA_BWD_D128_STDQ 2
+#endif
+#ifndef FA_BWD_D128_STKV
+#define FA_BWD_D128_STKV 2
+#endif
 template <int D> struct BwdCfg;
 template <> struct BwdCfg<64> {
-  static constexpr int BC = 64, BQ = 64, OCC_DQ = 2, OCC_KV = 2;
+  static constexpr int BC = FA_BWD_D64_BC, BQ = FA_BWD_D64_BQ, OCC_DQ = 2, OCC_KV = 2;
+  static constexpr int ST_DQ = FA_BWD_D64_STDQ, ST_KV = FA_BWD_D64_STKV;
 };
 template <> struct BwdCfg<128> {
-  static constexpr int BC = 64, BQ = 64, OCC_DQ = 2, OCC_KV = 1;
+  static constexpr int BC = FA_BWD_D128_BC, BQ = FA_BWD_D128_BQ, OCC_DQ = 2, OCC_KV = 1;
+  static constexpr int ST_DQ = FA_BWD_D128_STDQ, ST_KV = FA_BWD_D128_STKV;
 };
 template <> struct BwdCfg<256> {
-  static constexpr int BC = 32, BQ = 32, OCC_DQ = 1, OCC_KV = 1;
+  static constexpr int BC = 32, BQ = 32, OCC_DQ = 1, OCC_KV = 1, ST_DQ = 2, ST_KV = 2;
 };
-constexpr int kBwdST = 2;  // LDS ring stages (prefetch one tile ahead)
 
 // Per-lane LDS read geometry for tiles of 32-row blocks with D columns,
 // unpadded, 16-byte chunks XOR-swizzled by chunk_swz<D>.
@@ -85,14 +112,39 @@ template <int D> struct Geom {
 template <typename T, int D>
 __device__ __forceinline__ f32x16 mm_rows(const char* blk, const Geom<D>& G,
                                           const i32x4 (&b)[D / 16]) {
+  // Operands are read PF steps ahead of their MFMA: enough to cover LDS
+  // latency, few enough that two of these in flight do not crowd out the
+  // accumulators at d = 256.
+  constexpr int NS = D / 16, PF = NS < 4 ? NS : 4;
   f32x16 c;
 #pragma unroll
   for (int r = 0; r < 16; ++r) c[r] = 0.f;
-  i32x4 a[D / 16];
+  i32x4 a[NS];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) a[s] = *(const i32x4*)(blk + G.roff + (((2 * s) ^ G.ry) << 4));
+  for (int s = 0; s < PF; ++s) a[s] = *(const i32x4*)(blk + G.roff + (((2 * s) ^ G.ry) << 4));
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) c = Half<T>::mfma(a[s], b[s], c);
+  for (int s = 0; s < NS; ++s) {
+    if (s + PF < NS) a[s + PF] = *(const i32x4*)(blk + G.roff + (((2 * (s + PF)) ^ G.ry) << 4));
+    c = Half<T>::mfma(a[s], b[s], c);
+  }
+  return c;
+}
+
+// mm_rows with B read from LDS as well: row boff of a tile (lane l%32's
+// row), chunk (2 s + g) ^ by.
+template <typename T, int D>
+__device__ __forceinline__ f32x16 mm_rows_lds(const char* blk, const Geom<D>& G, const char* bt,
+                                              int boff, int by) {
+  constexpr int NS = D / 16;
+  f32x16 c;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c[r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const i32x4 a = *(const i32x4*)(blk + G.roff + (((2 * s) ^ G.ry) << 4));
+    const i32x4 b = *(const i32x4*)(bt + boff + (((2 * s) ^ by) << 4));
+    c = Half<T>::mfma(a, b, c);
+  }
   return c;
 }
 
@@ -110,14 +162,18 @@ __device__ __forceinline__ void mm_tr(const char* blk, const Geom<D>& G, const f
 #pragma unroll
     for (int e = 0; e < 4; ++e) xop[e] = (int)Half<T>::pack2(x[8 * h + 2 * e], x[8 * h + 2 * e + 1]);
     const char* hb = blk + 16 * h * 2 * D;
-    i16x4 lo[D / 32], hi[D / 32];
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b) {
+    // transposed reads issued TPF column blocks ahead of their MFMA
+    constexpr int NB = D / 32, TPF = NB < 4 ? NB : 4;
+    i16x4 lo[NB], hi[NB];
+    auto rd = [&](int b) __attribute__((always_inline)) {
       lo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(hb + G.toff[0] + (((4 * b) ^ G.tx[0]) << 4)));
       hi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(hb + G.toff[1] + (((4 * b) ^ G.tx[1]) << 4)));
-    }
+    };
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b) {
+    for (int b = 0; b < TPF; ++b) rd(b);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + TPF < NB) rd(b + TPF);
       const i16x8 a8 = {lo[b][0], lo[b][1], lo[b][2], lo[b][3], hi[b][0], hi[b][1], hi[b][2], hi[b][3]};
       acc[b] = Half<T>::mfma(__builtin_bit_cast(i32x4, a8), xop, acc[b]);
     }
@@ -155,7 +211,7 @@ __device__ __forceinline__ float hi16(int x, bool bf) {
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kBwdNW) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::OCC_DQ, BwdCfg<D>::OCC_DQ)))
 void bwd_dq(BwdParams p) {
-  constexpr int NW = kBwdNW, BR = 32 * NW, BC = BwdCfg<D>::BC, ST = kBwdST;
+  constexpr int NW = kBwdNW, BR = 32 * NW, BC = BwdCfg<D>::BC, ST = BwdCfg<D>::ST_DQ;
   constexpr int RB = 2 * D, TB = BC * RB, CPR = D / 8, CPT = BC * CPR / (64 * NW);
   constexpr int NS = D / 16, NKB = BC / 32, ND = D / 32;
   constexpr bool BF = __is_same(T, __bf16);
@@ -236,11 +292,18 @@ void bwd_dq(BwdParams p) {
     for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
   const float c = p.scale_log2;
 
-  issue_tile(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Ring of ST stages, prefetch distance PD = ST - 1: iteration j copies
+  // tile j + PD into the stage tile j - 1 used (everyone finished it before
+  // the last barrier) and ends once tile j + 1 has landed.  Copies complete
+  // in order, PT per tile and wave, so that is vmcnt <= PT * (tiles issued
+  // after j + 1).
+  constexpr int PD = ST - 1, PT = 2 * CPT;
+  static_assert(PT * (PD - 1) <= 31, "pending copies must fit wait_vmcnt");
+  for (int t = 0; t < PD && t < nt; ++t) issue_tile(t, t);
+  wait_vmcnt(PT * (min(PD, nt) - 1));
   __syncthreads();
   for (int j = 0; j < nt; ++j) {
-    if (j + 1 < nt) issue_tile(j + 1, (j + 1) % ST);
+    if (j + PD < nt) issue_tile(j + PD, (j + PD) % ST);
     if (j <= jlast) {
       const char* sk = smem + (j % ST) * 2 * TB;
       const char* sv = sk + TB;
@@ -250,18 +313,19 @@ void bwd_dq(BwdParams p) {
         const f32x16 dp = mm_rows<T, D>(sv + kb * 32 * RB, G, dop);
         // register r holds key key0 + 16 (r/8) + r%8
         const int key0 = j * BC + kb * 32 + 8 * g;
-        const bool need_mask = (j * BC + kb * 32 + 32 > N) || (CAUSAL && j * BC + kb * 32 + 31 > qrow0);
+        // visible iff 16 (r/8) + r%8 <= rel; rel >= 31 when no key of the
+        // block is hidden from this lane (one select per score, no branch)
         const int rel = (CAUSAL ? min(myq, N - 1) : N - 1) - key0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-          if (need_mask) pr = (16 * (r >> 3) + (r & 7) <= rel) ? pr : 0.f;
+          pr = (16 * (r >> 3) + (r & 7) <= rel) ? pr : 0.f;
           s[r] = pr * (dp[r] - dl);
         }
         mm_tr<T, D>(sk + kb * 32 * RB, G, s, acc);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt(PT * max(0, min(j + PD, nt - 1) - (j + 1)));
     __syncthreads();
   }
   if (myq < N) store_row<T, D>((T*)p.dq + head + (size_t)myq * D, acc, p.scale, g);
@@ -273,14 +337,18 @@ void bwd_dq(BwdParams p) {
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kBwdNW) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::OCC_KV, BwdCfg<D>::OCC_KV)))
 void bwd_dkdv(BwdParams p) {
-  constexpr int NW = kBwdNW, BK = 32 * NW, BQ = BwdCfg<D>::BQ, ST = kBwdST;
+  constexpr int NW = kBwdNW, BK = 32 * NW, BQ = BwdCfg<D>::BQ, ST = BwdCfg<D>::ST_KV;
   constexpr int RB = 2 * D, TB = BQ * RB, CPR = D / 8, CPT = BQ * CPR / (64 * NW);
   constexpr int NS = D / 16, NQB = BQ / 32, ND = D / 32;
   constexpr int SB = 2 * BQ * 4;          // row statistics per tile: base-2 lse, then D
   constexpr int STB = 2 * TB + SB;        // bytes per stage: Q, dO, statistics
   constexpr int SL = SB / 16 / NW;        // statistics chunks per wave
   static_assert(BQ * CPR % (64 * NW) == 0 && SB % (16 * NW) == 0 && SL <= 64, "tile split");
-  __shared__ __attribute__((aligned(1024))) char smem[ST * STB];
+  // At d = 256 the accumulators alone take 256 registers per lane; V's rows
+  // then live in LDS (read as B operands) instead of registers.
+  constexpr bool VLDS = D == 256;
+  constexpr int VB = VLDS ? BK * RB : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[ST * STB + VB];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
@@ -295,7 +363,7 @@ void bwd_dkdv(BwdParams p) {
 
   const int k0 = kblk * BK + w * 32;
   const int mykey = k0 + ql;
-  i32x4 kop[NS], vop[NS];
+  i32x4 kop[NS], vop[VLDS ? 1 : NS];
   {
     const size_t ro = kvhead + (size_t)min(mykey, N - 1) * D + 8 * g;
     const T* kr = (const T*)p.k + ro;
@@ -303,7 +371,20 @@ void bwd_dkdv(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       kop[s] = *(const i32x4*)(kr + 16 * s);
-      vop[s] = *(const i32x4*)(vr + 16 * s);
+      if constexpr (!VLDS) vop[s] = *(const i32x4*)(vr + 16 * s);
+    }
+  }
+  const char* vlds = smem + ST * STB;  // VLDS: the block's BK rows of V, chunk-swizzled
+  const int vboff = (w * 32 + ql) * RB, vby = g ^ chunk_swz<D>(ql);
+  if constexpr (VLDS) {
+    constexpr int CPV = BK * CPR / (64 * NW);
+    const uint32_t vdst = (uint32_t)(uintptr_t)(lds_void*)vlds;
+    const T* vb = (const T*)p.v + kvhead;
+#pragma unroll
+    for (int u = 0; u < CPV; ++u) {
+      const int sl = (u * NW + w) * 64 + lane, row = sl / CPR, cc = sl % CPR;
+      const size_t r = (size_t)min(kblk * BK + row, N - 1);
+      dma16(vb + r * D + (cc ^ chunk_swz<D>(row)) * 8, vdst + (u * NW + w) * 1024);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -351,20 +432,31 @@ void bwd_dkdv(BwdParams p) {
     for (int r = 0; r < 16; ++r) acck[d][r] = accv[d][r] = 0.f;
   const float c = p.scale_log2;
 
-  if (ntile > 0) issue_tile(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Ring as in bwd_dq; PT copies per tile and wave (the statistics chunk
+  // is one more instruction in every wave).
+  constexpr int PD = ST - 1, PT = 2 * CPT + 1;
+  static_assert(PT * (PD - 1) <= 31, "pending copies must fit wait_vmcnt");
+  for (int t = 0; t < PD && t < ntile; ++t) issue_tile(t, t);
+  wait_vmcnt(PT * (min(PD, ntile) - 1));
   __syncthreads();
   for (int j = 0; j < ntile; ++j) {
-    if (j + 1 < ntile) issue_tile(j + 1, (j + 1) % ST);
+    if (j + PD < ntile) issue_tile(j + PD, (j + PD) % ST);
     const int q0 = (qs + j % cnt) * BQ;
-    if (!CAUSAL || q0 + BQ - 1 >= k0) {  // else every query of the tile precedes every key of the wave
+    // Causal: skip a tile whose every query precedes every key of this wave
+    // (the mask would zero it).  Not at d = 256, where the branch around the
+    // accumulators costs the register allocator ~100 spilled registers; the
+    // masked tiles are computed and contribute zero there.
+    constexpr bool SKIP = CAUSAL && !VLDS;
+    if (!SKIP || q0 + BQ - 1 >= k0) {
       const char* sq = smem + (j % ST) * STB;
       const char* sd = sq + TB;
       const float* sst = (const float*)(sq + 2 * TB);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         f32x16 s = mm_rows<T, D>(sq + qb * 32 * RB, G, kop);
-        f32x16 dp = mm_rows<T, D>(sd + qb * 32 * RB, G, vop);
+        f32x16 dp;
+        if constexpr (VLDS) dp = mm_rows_lds<T, D>(sd + qb * 32 * RB, G, vlds, vboff, vby);
+        else dp = mm_rows<T, D>(sd + qb * 32 * RB, G, vop);
         // register r holds query q0 + 32 qb + 16 (r/8) + 8 g + r%8
         float l2[16], dd[16];
 #pragma unroll
@@ -377,12 +469,12 @@ void bwd_dkdv(BwdParams p) {
           dd[8 * hh + 0] = b0.x; dd[8 * hh + 1] = b0.y; dd[8 * hh + 2] = b0.z; dd[8 * hh + 3] = b0.w;
           dd[8 * hh + 4] = b1.x; dd[8 * hh + 5] = b1.y; dd[8 * hh + 6] = b1.z; dd[8 * hh + 7] = b1.w;
         }
-        const bool need_mask = CAUSAL && q0 + 32 * qb < k0 + 31;
-        const int lo = mykey - (q0 + 32 * qb + 8 * g);  // visible iff 16 (r/8) + r%8 >= lo
+        // causal: visible iff 16 (r/8) + r%8 >= lo (one select per score)
+        const int lo = mykey - (q0 + 32 * qb + 8 * g);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
-          if (need_mask) pr = (16 * (r >> 3) + (r & 7) >= lo) ? pr : 0.f;
+          if (CAUSAL) pr = (16 * (r >> 3) + (r & 7) >= lo) ? pr : 0.f;
           s[r] = pr;
           dp[r] = pr * (dp[r] - dd[r]);
         }
@@ -390,7 +482,7 @@ void bwd_dkdv(BwdParams p) {
         mm_tr<T, D>(sq + qb * 32 * RB, G, dp, acck);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt(PT * max(0, min(j + PD, ntile - 1) - (j + 1)));
     __syncthreads();
   }
   if (mykey < N) {

@@ -209,7 +209,7 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: fl
     _check(status)
 
 
-def attention_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+def attention_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
                   stream=None):
     """Allocate dq, dk, dv and the workspace with torch and run the backward pass.
     Returns (dq, dk, dv)."""

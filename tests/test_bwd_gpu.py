@@ -31,7 +31,7 @@ def _run(q, k, v, do, causal, scale):
     from io_aware_exact_05_amd import fa
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     o, lse = fa.attention(qd, kd, vd, bool(causal), scale)
-    dq, dk, dv = fa.attention_bwd(qd, kd, vd, o, lse, dod, bool(causal), scale)
+    dq, dk, dv = fa.attention_bwd(qd, kd, vd, o, dod, lse, bool(causal), scale)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu()
 
@@ -87,8 +87,8 @@ def test_deterministic():
     do = inputs.upstream_grad((2, 4, 500, 128), "bf16", 3).cuda()
     k, v = k[:, :2].contiguous(), v[:, :2].contiguous()
     o, lse = fa.attention(q, k, v, True, 0.088)
-    a = fa.attention_bwd(q, k, v, o, lse, do, True, 0.088)
-    b = fa.attention_bwd(q, k, v, o, lse, do, True, 0.088)
+    a = fa.attention_bwd(q, k, v, o, do, lse, True, 0.088)
+    b = fa.attention_bwd(q, k, v, o, do, lse, True, 0.088)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
