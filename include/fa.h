@@ -138,6 +138,35 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
 size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*
+ * fa_fwd_kvcache — attention of a short block of new queries against a long
+ * key/value cache (decoding), the KV-cache inference of "FlashAttention
+ * (HI)" (section on specialised solutions).  Same formula as fa_fwd with
+ * different query and key counts:
+ *   q, o    : [B,H,Nq,d] of dtype (FA_F16 or FA_BF16; others FA_ERR_DTYPE).
+ *   k, v    : the cache, [B,Hkv,Nkv,d] of dtype, Nkv >= Nq >= 1 (else
+ *             FA_ERR_SHAPE); K/V heads shared as in fa_fwd_gqa (Hkv = H:
+ *             one per query head).
+ *   lse     : output [B,H,Nq] fp32, natural-log logsumexp of each row.
+ *   causal  : 1 = the queries are the sequence's last Nq positions: query i
+ *             sees keys j <= Nkv - Nq + i (with Nq = 1, the whole cache).
+ *   workspace, workspace_bytes : device buffer of at least
+ *             fa_fwd_kvcache_workspace_bytes(...) bytes, 16-byte aligned,
+ *             owned by the caller, overwritten (partial results of the
+ *             cache chunks); may be NULL when that size is 0.
+ * The cache is cut into chunks processed by separate workgroups and merged
+ * exactly through their logsumexps; the cut depends only on the shape.
+ */
+int fa_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq,
+                   int Nkv, int d, int causal, float scale, int dtype, void* stream);
+
+/*
+ * Workspace bytes fa_fwd_kvcache needs for this shape (0 when the cache is
+ * not cut, and for invalid shapes).
+ */
+size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Hkv, int Nq, int Nkv, int d);
+
+/*
  * fa_fwd_fp8 — the same pass with OCP e4m3fn (finite-only, max 448) inputs,
  * the 8-bit path of "FlashAttention-3 (BN)" / "(FA)" (sections on new
  * hardware capabilities and on low precision).

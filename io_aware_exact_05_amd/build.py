@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["api.cpp", "fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip",
-           "fa_quant.hip", "fa_bwd.hip"]
+           "fa_quant.hip", "fa_bwd.hip", "fa_decode.hip"]
 # Extra flags per source.  fa_fwd_wide.hip keeps its MFMA accumulators in
 # VGPRs (VGPR form): its registers then fit two waves per SIMD with no copies
 # between the VGPR and AGPR files.

@@ -5,6 +5,7 @@
 // argument is reported without touching (or needing) a device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -13,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiMajor = 1, kAbiMinor = 2;
+constexpr int kAbiMajor = 1, kAbiMinor = 3;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -52,6 +53,29 @@ int check_shape(int B, int H, int N, int d) {
 
 // Rows per head of the backward workspace: N rounded up to 128.
 uint64_t bwd_npad(int N) { return ((uint64_t)N + 127) / 128 * 128; }
+
+// How attention over a key/value cache is cut: rows of a K/V group in
+// 32-row blocks, the cache in nsplit chunks (multiples of 128 keys, at least
+// 512 keys each) so that about 1024 workgroups run when the cache is long
+// enough.  Depends on the shape only, so the workspace size is known before
+// any device call.
+struct DecPlan {
+  int R, nrb, nsplit, chunk;
+};
+DecPlan dec_plan(int B, int H, int Hkv, int Nq, int Nkv) {
+  DecPlan d{};
+  d.R = (H / Hkv) * Nq;
+  d.nrb = (d.R + 31) / 32;
+  const uint64_t base = (uint64_t)B * Hkv * d.nrb;
+  const uint64_t max_split = std::max<uint64_t>(1, ((uint64_t)Nkv + 511) / 512);
+  const uint64_t want = std::max<uint64_t>(1, (1024 + base - 1) / base);
+  uint64_t ns = std::min(want, max_split);
+  const uint64_t per = ((uint64_t)Nkv + ns - 1) / ns;
+  const uint64_t chunk = (per + 127) / 128 * 128;
+  d.chunk = (int)chunk;
+  d.nsplit = (int)(((uint64_t)Nkv + chunk - 1) / chunk);
+  return d;
+}
 
 }  // namespace
 
@@ -184,6 +208,67 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int B, int H, int N, int d, int causal, float scale, int dtype, void* stream) {
   return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d,
                     causal, scale, dtype, stream);
+}
+
+size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Hkv, int Nq, int Nkv, int d) {
+  if (B < 1 || H < 1 || Hkv < 1 || Hkv > H || H % Hkv != 0 || Nq < 1 || Nkv < Nq || d < 1) return 0;
+  const DecPlan pl = dec_plan(B, H, Hkv, Nq, Nkv);
+  if (pl.nsplit == 1) return 0;
+  return (size_t)((uint64_t)B * H * Nq * pl.nsplit * ((uint64_t)d + 1) * 4);
+}
+
+int fa_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nkv,
+                   int d, int causal, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || Nq < 1 || Nkv < Nq) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_SHAPE;
+  if ((uint64_t)Nkv * d > (uint64_t)INT32_MAX || (uint64_t)B * H > (uint64_t)INT32_MAX)
+    return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
+  const DecPlan pl = dec_plan(B, H, Hkv, Nq, Nkv);
+  if ((uint64_t)B * Hkv * pl.nrb * pl.nsplit > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  const size_t need = fa_fwd_kvcache_workspace_bytes(B, H, Hkv, Nq, Nkv, d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return workspace ? FA_ERR_ARG : FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      (need > 0 && !aligned(workspace, 16)))
+    return FA_ERR_ALIGN;
+  const uint64_t rows = (uint64_t)B * H * Nq, kv_rows = (uint64_t)B * Hkv * Nkv;
+  const uint64_t eb = (uint64_t)d * 2;
+  const Range in[3] = {range_of(q, rows * eb), range_of(k, kv_rows * eb), range_of(v, kv_rows * eb)};
+  const Range out[3] = {range_of(o, rows * eb), range_of(lse, rows * 4), range_of(workspace, need)};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(out[i], out[j])) return FA_ERR_ALIAS;
+  }
+  fa::DecodeParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.ws_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.ws_lse = need > 0 ? p.ws_o + rows * pl.nsplit * (uint64_t)d : nullptr;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nkv = Nkv;
+  p.R = pl.R;
+  p.nrb = pl.nrb;
+  p.nsplit = pl.nsplit;
+  p.chunk = pl.chunk;
+  p.rows = rows;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  (void)hipGetLastError();
+  const hipError_t e = fa::launch_decode_half(p, d, causal, dtype == FA_BF16,
+                                              reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale,

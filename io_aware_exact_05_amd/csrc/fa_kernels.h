@@ -58,6 +58,33 @@ struct BwdParams {
   float scale_log2;  // scale * log2(e)
 };
 
+// Arguments of attention over a key/value cache (fa_decode.hip).  q, o:
+// [B*H*Nq, d] (rows of a head consecutive, heads of a K/V group consecutive);
+// k, v: [B*Hkv, Nkv, d]; lse [B*H*Nq].  The cache of each K/V head is cut
+// into nsplit chunks of `chunk` keys; with nsplit > 1 the partial results go
+// to ws_o [rows, nsplit, d] and ws_lse [rows, nsplit] (fp32) and a second
+// kernel merges them.
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+  int B;
+  int H;
+  int Hkv;
+  int Nq;
+  int Nkv;
+  int R;        // rows per K/V head: (H / Hkv) * Nq
+  int nrb;      // 32-row blocks per K/V head
+  int nsplit;
+  int chunk;    // keys per split
+  size_t rows;  // B * H * Nq
+  float scale_log2;
+};
+
 // Arguments of the fp8 forward: q8/k8/v8 e4m3fn [B*H, N, d], per-128-row
 // fp32 descales [B*H, nblk], o bf16 [B*H, N, d], lse fp32 [B*H, N].
 struct Fp8Params {
@@ -103,6 +130,8 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, int causal, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Params& p, int d, int causal, hipStream_t s);
 // Backward pass, fp16 / bf16 (fa_bwd.hip): bwd_dq then bwd_dkdv on stream s.
 hipError_t launch_bwd_half(const BwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
+// Attention over a key/value cache, fp16 / bf16, split over the cache.
+hipError_t launch_decode_half(const DecodeParams& p, int d, int causal, int is_bf16, hipStream_t s);
 // fp32 -> e4m3 block quantiser, optional randomised Hadamard rotation.
 hipError_t launch_quantize_e4m3(const QuantParams& p, int d, int rotate, hipStream_t s);
 

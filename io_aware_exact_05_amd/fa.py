@@ -28,8 +28,9 @@ STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_D
                 -7: "FA_ERR_ALIAS", -8: "FA_ERR_LAUNCH"}
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_bytes", "fa_fwd_fp8",
-           "fa_quantize_e4m3", "fa_status_string", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_bytes",
+           "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_fwd_fp8", "fa_quantize_e4m3",
+           "fa_status_string", "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -55,6 +56,10 @@ def _load():
     lib.fa_bwd_gqa.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_kvcache.restype = i
+    lib.fa_fwd_kvcache_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_kvcache_workspace_bytes.restype = sz
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_quantize_e4m3.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp]
@@ -222,6 +227,61 @@ def attention_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | No
     ws = torch.empty(bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=q.device)
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
     return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# attention over a key/value cache (decoding)
+# ----------------------------------------------------------------------------
+
+def kvcache_workspace_bytes(B: int, H: int, Hkv: int, Nq: int, Nkv: int, d: int) -> int:
+    return int(_lib.fa_fwd_kvcache_workspace_bytes(int(B), int(H), int(Hkv), int(Nq), int(Nkv),
+                                                   int(d)))
+
+
+def fa_fwd_kvcache_raw(q, k, v, o, lse, ws, ws_bytes, B, H, Hkv, Nq, Nkv, d, causal, scale, dtype,
+                       stream=0) -> int:
+    """Direct call of fa_fwd_kvcache with integer pointers; returns the status."""
+    return int(_lib.fa_fwd_kvcache(q, k, v, o, lse, ws, ws_bytes, int(B), int(H), int(Hkv),
+                                   int(Nq), int(Nkv), int(d), int(causal), float(scale),
+                                   int(dtype), stream))
+
+
+def fa_fwd_kvcache(q, k, v, o, lse, workspace, causal: bool, scale: float, stream=None) -> None:
+    """q, o [B,H,Nq,d]; k, v [B,Hkv,Nkv,d]; lse [B,H,Nq] fp32; workspace a uint8 device tensor
+    of at least kvcache_workspace_bytes(...) bytes (or None when that is 0)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
+        _dev(name, t)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("q, o must be [B, H, Nq, d] and k, v one [B, Hkv, Nkv, d] shape")
+    B, H, Nq, d = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k, v must be [B, Hkv, Nkv, d]")
+    if q.dtype not in (torch.float16, torch.bfloat16) or any(t.dtype != q.dtype for t in (k, v, o)):
+        raise ValueError("q, k, v, o must share float16 or bfloat16")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be float32 of shape [B, H, Nq]")
+    wp, wb = 0, 0
+    if workspace is not None:
+        _dev("workspace", workspace)
+        wp, wb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(fa_fwd_kvcache_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), wp or None, wb, B, H, Hkv, Nq, Nkv, d,
+                              int(bool(causal)), scale, DTYPE_CODE[q.dtype],
+                              _stream_handle(stream)))
+
+
+def attention_kvcache(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate o, lse and the workspace with torch and run fa_fwd_kvcache.  Returns (o, lse)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    B, H, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    nb = kvcache_workspace_bytes(B, H, k.shape[1], Nq, k.shape[2], d)
+    ws = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    fa_fwd_kvcache(q, k, v, o, lse, ws, causal, scale, stream)
+    return o, lse
 
 
 # ----------------------------------------------------------------------------

@@ -204,3 +204,48 @@ def test_bwd_gqa_invalid_heads(Hkv, code):
     a = _bwd_args()
     a["Hkv"] = Hkv
     assert fa.fa_bwd_gqa_raw(**a) == code
+
+
+# ----------------------- attention over a KV cache -------------------------
+KC = dict(zip(("q", "k", "v", "o", "lse", "ws"), (0x50000000 + i * 0x1000000 for i in range(6))))
+KB, KH, KHKV, KNQ, KNKV, KD = 2, 8, 2, 1, 40000, 128
+
+
+def _kv_args(**kw):
+    a = dict(KC, ws_bytes=fa.kvcache_workspace_bytes(KB, KH, KHKV, KNQ, KNKV, KD), B=KB, H=KH,
+             Hkv=KHKV, Nq=KNQ, Nkv=KNKV, d=KD, causal=0, scale=0.088, dtype=fa.FA_BF16)
+    a.update(kw)
+    return a
+
+
+def test_kvcache_workspace_bytes():
+    need = fa.kvcache_workspace_bytes(KB, KH, KHKV, KNQ, KNKV, KD)
+    assert need > 0 and need % (4 * (KD + 1) * KB * KH * KNQ) == 0
+    assert fa.kvcache_workspace_bytes(1, 1, 1, 1, 100, 64) == 0      # one chunk: no workspace
+    assert fa.kvcache_workspace_bytes(1, 1, 1, 5, 4, 64) == 0        # Nkv < Nq: invalid
+    assert fa.kvcache_workspace_bytes(1, 4, 3, 1, 100, 64) == 0      # Hkv does not divide H
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse", "ws"])
+def test_kvcache_null_pointer(which):
+    assert fa.fa_fwd_kvcache_raw(**_kv_args(**{which: 0})) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(Nq=0), -2), (dict(Nkv=0), -2), (dict(Nq=3, Nkv=2), -2),
+    (dict(Hkv=3), -2), (dict(Hkv=16), -2), (dict(Hkv=0), -2),
+    (dict(d=96), -4), (dict(dtype=fa.FA_F32), -3), (dict(dtype=fa.FA_E4M3), -3),
+    (dict(causal=2), -6), (dict(scale=float("nan")), -6),
+    (dict(ws_bytes=1), -6), (dict(q=KC["q"] + 8), -5), (dict(lse=KC["lse"] + 2), -5),
+    (dict(ws=KC["ws"] + 8), -5),
+    (dict(o=KC["k"]), -7), (dict(lse=KC["o"]), -7), (dict(ws=KC["v"]), -7), (dict(o=KC["ws"]), -7),
+])
+def test_kvcache_invalid_arguments(kw, code):
+    assert fa.fa_fwd_kvcache_raw(**_kv_args(**kw)) == code
+
+
+def test_kvcache_no_workspace_needed_accepts_null():
+    # one chunk (short cache): the workspace may be NULL; validation passes it,
+    # so check with an invalid dtype that validation reached the later checks
+    a = _kv_args(Nkv=300, ws=0, ws_bytes=0, causal=5)
+    assert fa.fa_fwd_kvcache_raw(**a) == -6

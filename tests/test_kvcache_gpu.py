@@ -1,0 +1,76 @@
+"""GPU parity of attention over a key/value cache (fa_fwd_kvcache through the
+C ABI) against the fp64 KV-cache oracle: every element, with the forward
+pass's gates (|O - O_ref| <= 1e-2 + half an output ulp, |LSE - LSE_ref| <=
+1e-3).  The shapes cover one and several cache chunks (split-KV merge),
+ragged cache lengths, query rows of a K/V group spanning several 32-row
+blocks, shared K/V heads, both maskings and every head dimension."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gates import check, widen
+from io_aware_exact_05_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _case(B, H, Hkv, Nq, Nkv, d, dtype, causal, seed, scale=None):
+    from io_aware_exact_05_amd import fa
+    q, _, _ = inputs.random_inputs(B, H, Nq, d, dtype, seed)
+    _, k, v = inputs.random_inputs(B, Hkv, Nkv, d, dtype, seed + 1)
+    scale = float(np.float32(1 / math.sqrt(d))) if scale is None else scale
+    o, lse = fa.attention_kvcache(q.cuda(), k.cuda(), v.cuda(), bool(causal), scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_kvcache(widen(q), widen(k), widen(v), causal, scale)
+    return check(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype,
+                 f"{dtype} B={B} H={H} Hkv={Hkv} Nq={Nq} Nkv={Nkv} d={d} causal={causal}")
+
+
+SHAPES = [  # B, H, Hkv, Nq, Nkv
+    (2, 4, 4, 1, 1), (2, 4, 4, 1, 100), (1, 8, 2, 1, 777), (2, 8, 1, 3, 1000),
+    (1, 4, 4, 16, 5000), (1, 16, 1, 5, 3001), (1, 2, 2, 64, 64), (3, 6, 3, 2, 20000),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("causal", [0, 1])
+def test_every_element(dtype, d, shape, causal):
+    _say(f"case kvcache dtype={dtype} d={d} shape={shape} causal={causal}")
+    B, H, Hkv, Nq, Nkv = shape
+    _case(B, H, Hkv, Nq, Nkv, d, dtype, causal, seed=Nkv + d)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_long_cache(causal):
+    # one decoded token per head against a 128K-token cache, grouped heads
+    _say(f"case kvcache long cache causal={causal}")
+    st = _case(1, 32, 8, 1, 131072, 128, "bf16", causal, seed=7)
+    _say(f"  {st}")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1.5])
+def test_unusual_scales(scale):
+    _say(f"case kvcache scale={scale}")
+    _case(1, 4, 2, 4, 2000, 128, "bf16", 1, seed=3, scale=scale)
+
+
+def test_matches_the_forward_kernel_when_lengths_are_equal():
+    from io_aware_exact_05_amd import fa
+    _say("case kvcache vs forward, Nq = Nkv")
+    q, k, v = (x.cuda() for x in inputs.random_inputs(1, 4, 200, 128, "bf16", 11))
+    o1, l1 = fa.attention_kvcache(q, k, v, True, 0.088)
+    o2, l2 = fa.attention(q, k, v, True, 0.088)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() < 2e-2
+    assert (l1 - l2).abs().max().item() < 1e-4
