@@ -101,6 +101,8 @@ def parse():
                     help="CPU-baseline budget; the sample is sized to about this")
     ap.add_argument("--profile-launches", type=int, default=0)
     ap.add_argument("--bwd", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time attention over a key/value cache (decoding shapes)")
     ap.add_argument("--copy-calib", action="store_true")
     return ap.parse_args()
 
@@ -130,6 +132,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n}))
         return
+
+    if args.decode:
+        return bench_decode(args, np, torch, fa, inputs, dev)
 
     cases = [w for w in inputs.WORKLOADS if w.config_id == args.config
              and (args.case is None or w.case_id == args.case)]
@@ -278,6 +283,106 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def bench_decode(args, np, torch, fa, inputs, dev):
+    """One step = one fa_fwd_kvcache call per decoding shape (every cache byte
+    read once).  The pass is bound by HBM: the roofline is algorithmic bytes
+    (Q, K, V read, O and the logsumexp written) over the launch time of the
+    call (its partial kernel and, when the cache is cut, the merge kernel)."""
+    stream = torch.cuda.current_stream()
+    cases = [w for w in inputs.DECODE_WORKLOADS if args.case is None or w.case_id == args.case]
+    if not cases:
+        sys.exit(f"no decoding workload case={args.case}")
+    parts, data = [], []
+    for w in cases:
+        q, k, v = inputs.decode_inputs(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        nb = fa.kvcache_workspace_bytes(w.B, w.H, w.Hkv, w.Nq, w.Nkv, w.d)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        data.append((w, (q, k, v)))
+        parts.append((w, lambda w=w, t=(qd, kd, vd, o, lse, ws):
+                      fa.fa_fwd_kvcache(*t, bool(w.causal), w.scale, stream)))
+    if args.profile_launches:
+        for _ in range(args.profile_launches):
+            for _, f in parts:
+                f()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_launches": args.profile_launches,
+                          "workload": [w.label() for w in cases]}))
+        return
+    for _ in range(args.warmup):
+        for _, f in parts:
+            f()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record(stream)
+        for i, (_, f) in enumerate(parts):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    step_bytes = sum(w.hbm_bytes for w in cases)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    per = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)] for i in range(len(parts))]
+    case_rep = {}
+    for i, (w, _) in enumerate(parts):
+        t = np.array(per[i])
+        gbs = w.hbm_bytes / (np.median(t) * 1e-3) / 1e9
+        case_rep[f"case{w.case_id}"] = {
+            "shape": w.label(), "ms_median": round(float(np.median(t)), 5),
+            "ms_min": round(float(t.min()), 5), "ms_p90": round(float(np.percentile(t, 90)), 5),
+            "hbm_gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "tflops": round(w.flops / (np.median(t) * 1e-3) / 1e12, 2)}
+    avg = [float(np.mean(t)) for t in per]
+    dom = int(np.argmax(avg))
+    wd = parts[dom][0]
+    achieved = wd.hbm_bytes / (avg[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": f"decode_partial+decode_merge {wd.label()}",
+                "avg_launch_ms": round(avg[dom], 5)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nbytes, t = 0.0, time.perf_counter()
+        for w, (q, k, v) in data:
+            oracle.attention_kvcache(q, k, v, w.causal, w.scale)
+            nbytes += w.hbm_bytes
+        dt = time.perf_counter() - t
+        cpu = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": _blas_threads(),
+               "kind": "oracle", "seconds": round(dt, 2),
+               "sample": "every head of every decoding shape of the step, fp64 numpy "
+                         "(one matrix-vector product per head)"}
+    w0 = cases[0]
+    out = {
+        "metric": "attention over a key/value cache: algorithmic HBM GB/s, 1 GPU",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w0.dtype, "data": "synthetic",
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "config": {"workload": w0.name, "shapes": [w.label() for w in cases],
+                   "step_bytes": step_bytes},
+        "cases": case_rep, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _blas_threads() -> int:
+    """Threads of numpy's BLAS, which runs the oracle's matrix products."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p["num_threads"] for p in threadpool_info() if p["user_api"] == "blas"],
+                   default=1)
+    except Exception:
+        return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
 def cpu_baseline(data, budget_s):
     """fp64 oracle on whole heads of the same workload, sized to ~budget_s."""
     import numpy as np
@@ -339,13 +444,7 @@ def cpu_baseline_bwd(data, budget_s):
             oracle.attention_bwd(q[bs, hs], k[bs, hs], v[bs, hs], do[bs, hs], w.causal, w.scale)
         flops += 2.5 * w.flops * take / n_heads
     dt = time.perf_counter() - t
-    try:  # threads of numpy's BLAS, which runs the matrix products
-        from threadpoolctl import threadpool_info
-        threads = max([p["num_threads"] for p in threadpool_info() if p["user_api"] == "blas"],
-                      default=1)
-    except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOPS", "cores": threads,
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOPS", "cores": _blas_threads(),
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{take} of {n_heads} heads (all {data[0][0].N} rows each) of every case "
                       f"of the step, fp64 numpy (BLAS threads for the matrix products)"}

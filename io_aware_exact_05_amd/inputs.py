@@ -14,7 +14,9 @@ Recipe (every workload is synthetic; no dataset is involved):
     entry of Q, K and V independently with probability 0.001 by 10;
   * round once: fp64 -> fp32 (numpy, round-to-nearest-even), then fp32 -> the
     storage dtype (torch, round-to-nearest-even).  The fp8 workload keeps the
-    fp32 values; quantising them is part of the method, not of the inputs.
+    fp32 values; quantising them is part of the method, not of the inputs;
+  * decoding (key/value cache) shapes draw Q [B,H,Nq,d], then K and V
+    [B,Hkv,Nkv,d], from ``SeedSequence([9000, case_id])``, rounded the same way.
 """
 from __future__ import annotations
 
@@ -128,3 +130,62 @@ def upstream_grad(shape, dtype: str, seed: int) -> torch.Tensor:
     """Seeded standard-normal upstream gradient dL/dO of the given shape (CPU, storage dtype)."""
     rng = np.random.default_rng(np.random.SeedSequence([4242, seed, *shape]))
     return _round(rng.standard_normal(tuple(shape)), dtype)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """A key/value-cache (decoding) shape: Nq new queries per query head
+    against Nkv cached keys and values per K/V head (Hkv heads, shared by
+    consecutive groups of H / Hkv query heads)."""
+    case_id: int
+    name: str
+    dtype: str
+    B: int
+    H: int
+    Hkv: int
+    Nq: int
+    Nkv: int
+    d: int
+    causal: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def hbm_bytes(self) -> float:
+        """Algorithmic HBM bytes of one pass: Q, K, V read once, O and the
+        fp32 logsumexp written once."""
+        b = 2
+        return (2.0 * self.B * self.H * self.Nq * self.d * b
+                + 2.0 * self.B * self.Hkv * self.Nkv * self.d * b
+                + 4.0 * self.B * self.H * self.Nq)
+
+    @property
+    def flops(self) -> float:
+        """4 * B * H * Nq * Nkv * d (the two products over every cached key)."""
+        return 4.0 * self.B * self.H * self.Nq * self.Nkv * self.d
+
+    def label(self) -> str:
+        c = "causal" if self.causal else "noncausal"
+        return (f"{self.name} B={self.B} H={self.H} Hkv={self.Hkv} Nq={self.Nq} "
+                f"Nkv={self.Nkv} d={self.d} {self.dtype} {c}")
+
+
+# One decoded token against the long-context cache (one K/V head per query
+# head), and four tokens at once against eight shared K/V heads per sequence.
+DECODE_WORKLOADS = [
+    DecodeWorkload(0, "decode_bf16", "bf16", 1, 32, 32, 1, 16384, 128, 1),
+    DecodeWorkload(1, "decode_bf16", "bf16", 8, 32, 8, 4, 16384, 128, 1),
+]
+
+
+def decode_inputs(w: DecodeWorkload):
+    """q [B,H,Nq,d], k, v [B,Hkv,Nkv,d] of the storage dtype (CPU): fp64
+    standard normals drawn in the order Q, K, V from
+    SeedSequence([9000, case_id]), rounded once as everywhere else."""
+    rng = np.random.default_rng(np.random.SeedSequence([9000, w.case_id]))
+    q = rng.standard_normal((w.B, w.H, w.Nq, w.d))
+    k = rng.standard_normal((w.B, w.Hkv, w.Nkv, w.d))
+    v = rng.standard_normal((w.B, w.Hkv, w.Nkv, w.d))
+    return _round(q, w.dtype), _round(k, w.dtype), _round(v, w.dtype)

@@ -74,3 +74,18 @@ def test_matches_the_forward_kernel_when_lengths_are_equal():
     torch.cuda.synchronize()
     assert (o1.float() - o2.float()).abs().max().item() < 2e-2
     assert (l1 - l2).abs().max().item() < 1e-4
+
+
+@pytest.mark.parametrize("case", [w.case_id for w in inputs.DECODE_WORKLOADS])
+def test_benchmark_decoding_shapes(case):
+    # the decoding shapes the benchmark times, same seeded inputs and the same
+    # entry point, every element against the oracle
+    from io_aware_exact_05_amd import fa
+    w = inputs.DECODE_WORKLOADS[case]
+    _say(f"case kvcache benchmark shape {w.label()}")
+    q, k, v = inputs.decode_inputs(w)
+    o, lse = fa.attention_kvcache(q.cuda(), k.cuda(), v.cuda(), bool(w.causal), w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_kvcache(widen(q), widen(k), widen(v), w.causal, w.scale)
+    st = check(o.cpu(), lse.cpu(), o_ref, lse_ref, w.dtype, w.label())
+    _say(f"  {st}")
