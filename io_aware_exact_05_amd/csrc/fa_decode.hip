@@ -266,37 +266,52 @@ void decode_partial(DecodeParams p) {
   }
 }
 
-// Combine the chunks' partial results of every row: one wave per row, lane
-// l owning columns [l * D / 64, + D / 64) (one column at d = 64).
+// Combine the chunks' partial results of every row, one wave per row.  The
+// wave's lanes form 64 / (D / 8) groups that walk the chunks side by side,
+// lane l of a group owning columns [8 (l % (D / 8)), + 8); every chunk's O is
+// read as two 16-byte loads per lane, the loads of several chunks are in
+// flight together, and the groups' sums meet through lane shuffles in a fixed
+// order (so results are the same run to run).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge(DecodeParams p) {
-  constexpr int CPL = D / 64;
-  static_assert(CPL == 1 || CPL % 2 == 0, "columns per lane: one or pairs");
+  constexpr int LPC = D / 8;   // lanes covering one row
+  constexpr int NG = 64 / LPC; // chunks read side by side
   const int lane = threadIdx.x & 63;
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= p.rows) return;
-  const float* ls = p.ws_lse + row * p.nsplit;
+  const int ns = p.nsplit;
+  const float* ls = p.ws_lse + row * ns;
   float M = kNegInf;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, ls[s]);
-  float acc[CPL], L = 0.f;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ls[s]);
 #pragma unroll
-  for (int cc = 0; cc < CPL; ++cc) acc[cc] = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float ws = ls[s] == kNegInf ? 0.f : __expf(ls[s] - M);
-    L += ws;
-    const float* src = p.ws_o + (row * p.nsplit + s) * D + lane * CPL;
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const int grp = lane / LPC, c0 = (lane % LPC) * 8;
+  float acc[8], L = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) acc[cc] += ws * src[cc];
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const float* base = p.ws_o + row * ns * D + c0;
+#pragma unroll 4
+  for (int s = grp; s < ns; s += NG) {
+    const float l_s = ls[s];
+    const float4 a = *(const float4*)(base + (size_t)s * D);
+    const float4 b = *(const float4*)(base + (size_t)s * D + 4);
+    const float w = l_s == kNegInf ? 0.f : __expf(l_s - M);
+    L += w;
+    acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+    acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
   }
+#pragma unroll
+  for (int off = LPC; off < 64; off <<= 1) {
+    L += __shfl_xor(L, off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+  }
+  if (grp != 0) return;
   const float inv = 1.0f / L;  // L >= 1: the chunk holding the maximum has weight 1
-  T* out = (T*)p.o + row * D + lane * CPL;
-  if constexpr (CPL == 1) {  // d = 64: one column per lane, a 16-bit store
-    *(uint16_t*)out = (uint16_t)(Half<T>::pack2(acc[0] * inv, 0.f) & 0xffffu);
-  } else {
+  i32x4 pk;
 #pragma unroll
-    for (int cc = 0; cc < CPL; cc += 2)
-      *(uint32_t*)(out + cc) = Half<T>::pack2(acc[cc] * inv, acc[cc + 1] * inv);
-  }
+  for (int e = 0; e < 4; ++e) pk[e] = (int)Half<T>::pack2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *(i32x4*)((T*)p.o + row * D + c0) = pk;
   if (lane == 0) p.lse[row] = M + __logf(L);
 }
 
