@@ -136,8 +136,12 @@ def main():
     if args.decode:
         return bench_decode(args, np, torch, fa, inputs, dev)
 
-    cases = [w for w in inputs.WORKLOADS if w.config_id == args.config
-             and (args.case is None or w.case_id == args.case)]
+    # the fp8 configuration is one case; its head-dimension and causal
+    # variants run only when named with --case
+    pool = inputs.WORKLOADS + inputs.FP8_VARIANTS
+    cases = [w for w in pool if w.config_id == args.config
+             and (w.case_id == args.case if args.case is not None
+                  else (w.config_id != 5 or w.case_id == 0))]
     if not cases:
         sys.exit(f"no workload config={args.config} case={args.case}")
     fp8 = cases[0].dtype == "e4m3"

@@ -181,7 +181,8 @@ size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Hkv, int Nq, int Nkv, in
  *   o_bf16               : output [B,H,N,d] bfloat16.
  *   lse                  : output [B,H,N] fp32, natural-log logsumexp of the
  *                          scaled scores of the dequantised inputs.
- *   causal, scale        : as in fa_fwd.  d must be 128 (else FA_ERR_HEADDIM).
+ *   causal, scale, d     : as in fa_fwd (d in {64, 128, 256}, else
+ *                          FA_ERR_HEADDIM).
  * P is rounded to e4m3 for the second product; before rounding it is scaled
  * by 2^6 (and by the non-power-of-two part of the V descale), which keeps it
  * <= 256 (no saturation) and mostly above e4m3's subnormal range.

@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiMajor = 1, kAbiMinor = 3;
+constexpr int kAbiMajor = 1, kAbiMinor = 4;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -278,7 +278,6 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_de
     return FA_ERR_NULL;
   const int sc = check_shape(B, H, N, d);
   if (sc != FA_OK) return sc;
-  if (d != 128) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (!std::isfinite(scale)) return FA_ERR_ARG;
   if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o_bf16, 16) ||

@@ -8,7 +8,8 @@
 // Same tiling and online softmax as the 16-bit kernel: each wave owns 32
 // query rows (within one descale block), a workgroup of 8 (4 with causal
 // masking) waves 256 (128) rows; K/V tiles of 128 rows (one descale block
-// each) stream through an LDS ring filled by direct global -> LDS copies;
+// each; 64 rows, half a block, at d = 256) stream through an LDS ring filled
+// by direct global -> LDS copies; d is 64, 128 or 256;
 // S^T = K8 Q8^T keeps one query per lane.
 //   scores    t = s8 * (scale log2 e * q_descale[query block] *
 //             k_descale[tile]): one per-tile multiplier folded into the FMA.
@@ -43,12 +44,22 @@ typedef i32x2 __attribute__((address_space(3))) lds_i32x2;
 
 constexpr float kLazy8 = 2.0f;  // log2 headroom of the running max on this path
 
-// XOR swizzle of the 16-byte chunk inside a 128-byte fp8 row (two rows per
-// 256-byte bank line): for the K reads (16 rows, one chunk) every
-// (row parity, chunk) pair is distinct, and for the transposed V reads
-// (8 consecutive rows x 2 adjacent chunks per half-wave) so is every one of
-// the 16 (row, chunk) pairs.
-__device__ __forceinline__ int swz8(int row) { return (((row >> 1) & 3) << 1) | ((row >> 3) & 1); }
+// XOR swizzle of the 16-byte chunk inside an fp8 row of D bytes; the value
+// is below D / 16, so XOR with it permutes the row's chunks.
+//   D = 128 (two rows per 256-byte bank line): for the K reads (16 rows, one
+//     chunk) every (row parity, chunk) pair is distinct, and for the
+//     transposed V reads (8 consecutive rows x 2 adjacent chunks per
+//     half-wave) so is every one of the 16 (row, chunk) pairs.
+//   D = 64 (four rows per line): rows r, r + 4, r + 8, r + 12, which share
+//     their place in the line, get distinct chunks.
+//   D = 256 (one row per line): the swizzle of 256-byte rows of the 16-bit
+//     kernels (chunk_swz<128>).
+template <int D>
+__device__ __forceinline__ int swz8(int row) {
+  if constexpr (D == 64) return (row >> 2) & 3;
+  else if constexpr (D == 128) return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  else return chunk_swz<128>(row);
+}
 
 __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
   // format 0 (e4m3) for both operands, E8M0 block scales 127 = 2^0
@@ -70,24 +81,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Key-tile rows (64 or 128) and waves per SIMD (tuning builds may override
-// them).  Measured: 128-key tiles beat 64-key tiles (about 12%).  Waves per
-// workgroup NW: 8 without masking (the two halves of the workgroup, waves w
-// and w + 4 sharing a SIMD, run half a tile apart: +5%), 4 with causal
-// masking (more, smaller workgroups balance the unequal causal tiles).
+// Key-tile rows (64 or 128) per head dimension and waves per SIMD (tuning
+// builds may override them).  Measured at d = 128: 128-key tiles beat 64-key
+// tiles (about 12%).  At d = 256 a 128-key score tile (64 registers) next to
+// O (128) and Q (32) does not fit two waves per SIMD, so tiles are 64 keys.
+// Waves per workgroup NW: 8 without masking (the two halves of the
+// workgroup, waves w and w + 4 sharing a SIMD, run half a tile apart: +5%),
+// 4 with causal masking (more, smaller workgroups balance the unequal causal
+// tiles).
 #ifndef FA_FP8_BC
 #define FA_FP8_BC 128
 #endif
 #ifndef FA_FP8_OCC
 #define FA_FP8_OCC 2
 #endif
+template <int D> constexpr int fp8_bc() { return D == 256 ? 64 : FA_FP8_BC; }
 template <bool CAUSAL> constexpr int fp8_nw() { return CAUSAL ? 4 : 8; }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * fp8_nw<CAUSAL>()) __attribute__((amdgpu_waves_per_eu(FA_FP8_OCC, FA_FP8_OCC)))
 void fwd_fp8(Fp8Params p) {
   constexpr int NW = fp8_nw<CAUSAL>();
-  constexpr int D = 128, BC = FA_FP8_BC, BR = 32 * NW, ST = NW == 8 ? 4 : 2;
+  constexpr int BC = fp8_bc<D>(), BR = 32 * NW, ST = NW == 8 ? 4 : 2;
   constexpr bool PP = NW == 8;
   constexpr int PD = PP ? ST - 2 : ST - 1;   // tiles copied ahead
   constexpr int RB = D;                      // bytes per fp8 row
@@ -135,13 +150,13 @@ void fwd_fp8(Fp8Params p) {
   // last tile this wave computes (-1: all its rows are past N)
   const int jlast = qrow0 >= N ? -1 : (CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1);
 
-  // ---- copies (as in the 16-bit kernel, 128-byte rows) ----
+  // ---- copies (as in the 16-bit kernel, D-byte rows) ----
   int ld_row[CPT], ld_off[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int s = (u * NW + w) * 64 + lane, row = s / CPR, ch16 = s % CPR;
     ld_row[u] = row;
-    ld_off[u] = (ch16 ^ swz8(row)) * 16;
+    ld_off[u] = (ch16 ^ swz8<D>(row)) * 16;
   }
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
   auto issue_tile = [&](int j) __attribute__((always_inline)) {
@@ -157,13 +172,13 @@ void fwd_fp8(Fp8Params p) {
   // K operand (A of S^T): row kb*32 + swap_bits23(ql), logical chunks
   // 4 s + 2 g and 4 s + 2 g + 1.
   const int krow = swap_bits23(ql);
-  const int kx = swz8(krow);
+  const int kx = swz8<D>(krow);
   // V operand (A of O^T = V^T P~^T), transposed byte reads: lane r of each
   // 16-lane group addresses row 32 kb + 16 h + 8 g + r/2, chunk 2 b + lane/16 % 2,
   // byte 8 (r % 2) of that chunk.
   const int tr = (lane & 15) >> 1;
   const int vrow_off = (8 * g + tr) * RB + 8 * (lane & 1);
-  const int vx = ((lane >> 4) & 1) ^ swz8(8 * g + tr);
+  const int vx = ((lane >> 4) & 1) ^ swz8<D>(8 * g + tr);
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -302,8 +317,14 @@ void fwd_fp8(Fp8Params p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qop[s][e] ^= flip;
     }
+    // drain: Q and the first tiles (16-byte register operands, which the
+    // host pass of a kernel template also accepts)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qop[s]));
+    for (int s = 0; s < NS; ++s) {
+      const i32x4 a = {qop[s][0], qop[s][1], qop[s][2], qop[s][3]};
+      const i32x4 b = {qop[s][4], qop[s][5], qop[s][6], qop[s][7]};
+      asm volatile("" ::"v"(a), "v"(b));
+    }
   }
   wait_vmcnt(0);
   __syncthreads();
@@ -350,7 +371,7 @@ void fwd_fp8(Fp8Params p) {
   // ---- epilogue: O = O~ 2^(lazy - 8) / l, LSE = ln2 (m + log2 l) ----
   // A lane holds one query's O row in 8-byte pieces; each wave stages its 32
   // bf16 rows in LDS (the ring is idle after the last barrier) and writes
-  // whole 256-byte rows, 16-byte chunks XOR-swizzled by row.
+  // whole 2D-byte rows, 16-byte chunks XOR-swizzled by row.
   constexpr int ORB = D * 2, OCPR = ORB / 16;
   static_assert(NW * 32 * ORB <= ST * SB, "staging fits in the ring");
   char* stg = smem + w * (32 * ORB);
@@ -378,19 +399,28 @@ void fwd_fp8(Fp8Params p) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_fwd_fp8(const Fp8Params& p, int d, int causal, hipStream_t s) {
-  if (d != 128) return hipErrorInvalidValue;
+template <int D>
+hipError_t launch_fp8_d(const Fp8Params& p, int causal, hipStream_t s) {
   const int nw = causal ? fp8_nw<true>() : fp8_nw<false>();
   Fp8Params q = p;
   q.nq = (p.N + 32 * nw - 1) / (32 * nw);
   const unsigned grid = (unsigned)(q.nq * p.BH);
   if (causal)
-    hipLaunchKernelGGL((fwd_fp8<true>), dim3(grid), dim3(64 * nw), 0, s, q);
+    hipLaunchKernelGGL((fwd_fp8<D, true>), dim3(grid), dim3(64 * nw), 0, s, q);
   else
-    hipLaunchKernelGGL((fwd_fp8<false>), dim3(grid), dim3(64 * nw), 0, s, q);
+    hipLaunchKernelGGL((fwd_fp8<D, false>), dim3(grid), dim3(64 * nw), 0, s, q);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, int causal, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_fp8_d<64>(p, causal, s);
+    case 128: return launch_fp8_d<128>(p, causal, s);
+    case 256: return launch_fp8_d<256>(p, causal, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

@@ -77,8 +77,18 @@ WORKLOADS = [
 ]
 
 
+# Variants of the fp8 workload (same distribution and sizes): the other head
+# dimensions and causal masking.  Not part of the five configurations; the
+# benchmark runs them only when asked for by case.
+FP8_VARIANTS = [
+    Workload(5, 1, "fp8_outliers_d64", "e4m3", 4, 16, 4096, 64, 0, "entries_x10"),
+    Workload(5, 2, "fp8_outliers_d256", "e4m3", 4, 16, 4096, 256, 0, "entries_x10"),
+    Workload(5, 3, "fp8_outliers_causal", "e4m3", 4, 16, 4096, 128, 1, "entries_x10"),
+]
+
+
 def workload(config_id: int, case_id: int = 0) -> Workload:
-    for w in WORKLOADS:
+    for w in WORKLOADS + FP8_VARIANTS:
         if w.config_id == config_id and w.case_id == case_id:
             return w
     raise KeyError((config_id, case_id))

@@ -127,7 +127,7 @@ def test_fp8_null_pointer(which):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=64), -4), (dict(d=256), -4), (dict(d=100), -4), (dict(N=0), -2), (dict(H=0), -2),
+    (dict(d=32), -4), (dict(d=512), -4), (dict(d=100), -4), (dict(N=0), -2), (dict(H=0), -2),
     (dict(causal=5), -6), (dict(scale=float("nan")), -6),
     (dict(q8=Q + 4), -5), (dict(o=O + 2), -5), (dict(kd=KD + 2), -5),
     (dict(o=Q), -7), (dict(lse=QD), -7), (dict(o=VD - 64), -7),

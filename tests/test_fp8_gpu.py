@@ -25,6 +25,11 @@ from oracle import quant_oracle as qo
 pytestmark = pytest.mark.gpu
 
 REL_RMSE_GATE = 5e-2
+# End-to-end bound for the d = 64, d = 256 and causal variants of the fp8
+# workload, which the stated gate does not cover.  At d = 64 the rotation
+# spreads an outlier over 64 columns instead of 128, so the block amax (and
+# with it the code step) stays larger: 0.058 measured with rotation.
+VARIANT_REL_RMSE = 1e-1
 
 
 def _fa():
@@ -123,16 +128,17 @@ def _fp8_kernel_bounds(Qd, Kd, Vd, causal, scale, o_ref, lse_ref):
     return o_tol, lse_tol
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 7, 129, 300, 1000])
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("rotate", [True, False])
-def test_fp8_kernel_on_oracle_quantised_inputs(N, causal, rotate):
+def test_fp8_kernel_on_oracle_quantised_inputs(d, N, causal, rotate):
     """The attention kernel alone: Q, K, V are quantised by the oracle (with
     the rotation when asked), the kernel gets those codes and descales, and
     the fp64 oracle runs on exactly the values the codes stand for."""
-    _say(f"case fp8 kernel N={N} causal={causal} rotate={rotate}")
+    _say(f"case fp8 kernel d={d} N={N} causal={causal} rotate={rotate}")
     fa = _fa()
-    B, H, d = 1, 2, 128
+    B, H = 1, 2
     q, k, v = _fp32_inputs(B, H, N, d, seed=N + 11)
     scale = float(np.float32(1 / math.sqrt(d)))
     signs = inputs.rotation_signs(d, seed=2).numpy() if rotate else None
@@ -157,14 +163,15 @@ def test_fp8_kernel_on_oracle_quantised_inputs(N, causal, rotate):
     assert ro <= 1.0 and rl <= 1.0
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [0, 1])
-def test_fp8_attention_exactly_representable_inputs(causal):
+def test_fp8_attention_exactly_representable_inputs(d, causal):
     """Values in {0, +-1/2, +-1} with one 8 per block and column are quantised
     without error (the descale 2^-5 maps them onto the e4m3 codes of 0, 16,
     32 and 256), so the end-to-end result obeys the kernel-only bounds."""
-    _say(f"case fp8 exact inputs causal={causal}")
+    _say(f"case fp8 exact inputs d={d} causal={causal}")
     fa = _fa()
-    B, H, N, d = 1, 2, 384, 128
+    B, H, N = 1, 2, 384
     rng = np.random.default_rng(5)
     vals = np.array([-1.0, -0.5, 0.0, 0.5, 1.0], np.float32)
     qkv = []
@@ -201,8 +208,10 @@ def _sample_rows(B, H, N, seed, per_head=24, heads=6):
     return np.array(rows, np.int64)
 
 
-def test_fp8_workload_rotation_and_without():
-    w = inputs.workload(5, 0)
+@pytest.mark.parametrize("case", [0, 1, 2, 3])
+def test_fp8_workload_rotation_and_without(case):
+    # case 0 is the fp8 configuration; 1-3 its d = 64, d = 256 and causal variants
+    w = inputs.workload(5, case)
     _say(f"case fp8 workload {w.label()}")
     fa = _fa()
     q, k, v = inputs.workload_inputs(w)
@@ -221,13 +230,22 @@ def test_fp8_workload_rotation_and_without():
     _say(f"  rel-RMSE with rotation {errs[True][0]:.4f} (max|dLSE| {errs[True][1]:.4f}); "
          f"without {errs[False][0]:.4f} (max|dLSE| {errs[False][1]:.4f}); "
          f"ratio {errs[False][0] / errs[True][0]:.2f}")
-    assert errs[True][0] <= REL_RMSE_GATE
+    if case == 0:  # the fp8 configuration: the stated 5e-2 gate
+        assert errs[True][0] <= REL_RMSE_GATE
+    else:
+        # variants of it: their kernel arithmetic is gated element by element
+        # above (test_fp8_kernel_on_oracle_quantised_inputs); end to end the
+        # quantisation error is reported, bounded loosely, and the rotation
+        # must not make it worse
+        assert errs[True][0] <= VARIANT_REL_RMSE
+        assert errs[True][0] <= errs[False][0]
 
 
-def test_fp8_deterministic_and_fully_written():
-    _say("case fp8 determinism/poison")
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_deterministic_and_fully_written(d):
+    _say(f"case fp8 determinism/poison d={d}")
     fa = _fa()
-    B, H, N, d = 1, 3, 333, 128
+    B, H, N = 1, 3, 333
     q, k, v = _fp32_inputs(B, H, N, d, seed=77)
     q8, qd = fa.quantize_e4m3(q.cuda(), True)
     k8, kd = fa.quantize_e4m3(k.cuda(), True)
