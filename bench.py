@@ -224,6 +224,7 @@ def main():
     fmul = 2.5 if args.bwd else 1.0
     ms_step = (t1 - t0) * 1e3 / K
     per_part_ms = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)] for i in range(len(parts))]
+    cold_ms = cold_runs(torch, dev, stream, parts, launch)
     step_flops = sum(w.flops for w, _ in data) * fmul
     value = step_flops / (ms_step * 1e-3) / 1e12
     dtype = cases[0].dtype
@@ -233,7 +234,7 @@ def main():
     for i, (nm, w, _) in enumerate(parts):
         t = np.array(per_part_ms[i])
         rep_i = {"ms_median": round(float(np.median(t)), 5), "ms_min": round(float(t.min()), 5),
-                 "ms_p90": round(float(np.percentile(t, 90)), 5)}
+                 "ms_p90": round(float(np.percentile(t, 90)), 5), "ms_cold": round(cold_ms[i], 5)}
         if w is not None:
             tf = fmul * w.flops / (np.median(t) * 1e-3) / 1e12
             rep_i.update(tflops=round(tf, 2), pct_of_peak=round(100 * tf / peak, 2))
@@ -360,7 +361,7 @@ def bench_decode(args, np, torch, fa, inputs, dev):
             nbytes += w.hbm_bytes
         dt = time.perf_counter() - t
         cpu = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": _blas_threads(),
-               "kind": "oracle", "seconds": round(dt, 2),
+               "kind": "oracle", "seconds": round(dt, 2), "cpu_model": cpu_model(),
                "sample": "every head of every decoding shape of the step, fp64 numpy "
                          "(one matrix-vector product per head)"}
     w0 = cases[0]
@@ -375,6 +376,35 @@ def bench_decode(args, np, torch, fa, inputs, dev):
         "cases": case_rep, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def cold_runs(torch, dev, stream, parts, launch):
+    """Diagnostic, outside the timed steps: each launch once more right after
+    writing 512 MiB of other memory, so that its inputs are no longer held in
+    the L2 caches or the Infinity Cache.  Returns one time (ms) per launch."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = []
+    for i in range(len(parts)):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    del flush
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _blas_threads() -> int:
@@ -418,7 +448,7 @@ def cpu_baseline(data, budget_s):
         flops += w.flops * take / n_heads
     dt = time.perf_counter() - t
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOPS", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 2),
+            "kind": "oracle", "seconds": round(dt, 2), "cpu_model": cpu_model(),
             "sample": f"{take} of {n_heads} heads (all {data[0][0].N} rows each) of every case "
                       f"of the step, fp64, OpenMP over query rows"}
 
@@ -449,7 +479,7 @@ def cpu_baseline_bwd(data, budget_s):
         flops += 2.5 * w.flops * take / n_heads
     dt = time.perf_counter() - t
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOPS", "cores": _blas_threads(),
-            "kind": "oracle", "seconds": round(dt, 2),
+            "kind": "oracle", "seconds": round(dt, 2), "cpu_model": cpu_model(),
             "sample": f"{take} of {n_heads} heads (all {data[0][0].N} rows each) of every case "
                       f"of the step, fp64 numpy (BLAS threads for the matrix products)"}
 
