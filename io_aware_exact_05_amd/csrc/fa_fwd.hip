@@ -414,23 +414,29 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 // Causal work per query tile grows with the tile index.  fwd_wide runs a few
 // 4-wave workgroups per CU; when its whole grid fits in one round of those
 // slots the heaviest tiles alone set the runtime, and fwd_mfma16 (one 8-wave
-// workgroup per CU, more rounds, heaviest tiles first) balances better.
-static bool use_wide(const FwdParams& p, int d, int causal) {
+// workgroup per CU, more rounds, heaviest tiles first) balances better.  With
+// at least two rounds of the long-causal configuration's 512-row workgroups
+// (one per CU) those balance too, and its 64-row waves run faster.
+// Returns 0 (fwd_mfma16), 1 (fwd_wide) or 2 (fwd_wide, long causal).
+static int wide_kind(const FwdParams& p, int d, int causal) {
   const bool enabled = d == 64 ? FA_D64_WIDE : d == 128 ? FA_D128_WIDE : FA_D256_WIDE;
-  if (!enabled) return false;
-  if (!causal) return true;
+  if (!enabled) return 0;
+  if (!causal) return 1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
+  const int lr = wide_long_causal_rows(d);
+  if (lr > 0 && (long long)((p.N + lr - 1) / lr) * p.BH >= 2LL * cus) return 2;
   const int br = wide_rows_per_block(d, causal);
   const long long grid = (long long)((p.N + br - 1) / br) * p.BH;
-  return grid > (long long)wide_blocks_per_cu(d, causal) * cus;
+  return grid > (long long)wide_blocks_per_cu(d, causal) * cus ? 1 : 0;
 }
 
 template <typename T>
 static hipError_t launch_t(const FwdParams& p, int d, int causal, hipStream_t s) {
-  if (use_wide(p, d, causal)) return launch_fwd_wide(p, d, causal, std::is_same<T, __bf16>::value, s);
+  const int kind = wide_kind(p, d, causal);
+  if (kind) return launch_fwd_wide(p, d, causal, kind == 2, std::is_same<T, __bf16>::value, s);
   switch (d) {
     case 64:  return causal ? launch_one<T, 64, true>(p, s) : launch_one<T, 64, false>(p, s);
     case 128: return causal ? launch_one<T, 128, true>(p, s) : launch_one<T, 128, false>(p, s);

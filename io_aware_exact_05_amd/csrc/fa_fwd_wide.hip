@@ -71,12 +71,16 @@ constexpr bool swz_step4_is_xor1() {
 //           3.5-5% over two uncoordinated 4-wave workgroups);
 //   d = 128 causal: 32 rows per wave at three waves per SIMD (twice as many
 //           workgroups, so the unequal causal tiles balance over rounds);
+//   d = 128 causal with many query tiles (LONG: at least two rounds of
+//           512-row workgroups, one per CU): the non-causal configuration,
+//           whose heavy-first rounds then balance (6-8% over the 32-row
+//           kernel at 4096-16384 tokens);
 //   d = 256: 32 rows per wave, one 8-wave workgroup per CU with ping-pong
 //           halves (+1-2% over two 4-wave workgroups);
 //   d = 64: 64 rows per wave and 64-key tiles (the state is small), one
 //           8-wave workgroup per CU with ping-pong halves (+10-12% over the
 //           32-row 8-wave kernel).
-template <int D, bool CAUSAL> struct WideCfg;
+template <int D, bool CAUSAL, bool LONG = false> struct WideCfg;
 template <bool C> struct WideCfg<64, C> {
   static constexpr int QB = 2, BC = 64, ST = 3, OCC = 2, NW = 8;
   static constexpr bool XK = false, XV = false;
@@ -89,6 +93,10 @@ template <> struct WideCfg<128, true> {
   static constexpr int QB = 1, BC = 32, ST = 3, OCC = 3;
   static constexpr bool XK = false, XV = false;
 };
+template <> struct WideCfg<128, true, true> {
+  static constexpr int QB = 2, BC = 32, ST = 4, OCC = 2, NW = 8;
+  static constexpr bool XK = false, XV = false;
+};
 template <bool C> struct WideCfg<256, C> {
   static constexpr int QB = 1, BC = 32, ST = 4, OCC = 2, NW = 8;
   static constexpr bool XK = true, XV = true;
@@ -97,11 +105,11 @@ template <bool C> struct WideCfg<256, C> {
 // Waves per workgroup: 4 unless the configuration names 8 (ping-pong halves).
 template <typename C, typename = void> struct NWOf { static constexpr int v = 4; };
 template <typename C> struct NWOf<C, std::void_t<decltype(C::NW)>> { static constexpr int v = C::NW; };
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__((64 * NWOf<WideCfg<D, CAUSAL>>::v))
-__attribute__((amdgpu_waves_per_eu(WideCfg<D, CAUSAL>::OCC, WideCfg<D, CAUSAL>::OCC)))
+template <typename T, int D, bool CAUSAL, bool LONG>
+__global__ __launch_bounds__((64 * NWOf<WideCfg<D, CAUSAL, LONG>>::v))
+__attribute__((amdgpu_waves_per_eu(WideCfg<D, CAUSAL, LONG>::OCC, WideCfg<D, CAUSAL, LONG>::OCC)))
 void fwd_wide(FwdParams p) {
-  using Cfg = WideCfg<D, CAUSAL>;
+  using Cfg = WideCfg<D, CAUSAL, LONG>;
   constexpr int NW = NWOf<Cfg>::v;
   constexpr bool PP = NW == 8;
   constexpr int BC = Cfg::BC, QB = Cfg::QB, WR = 32 * QB, BR = WR * NW;
@@ -456,22 +464,24 @@ void fwd_wide(FwdParams p) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool LONG = false>
 hipError_t launch_wide(const FwdParams& p, hipStream_t stream) {
-  constexpr int NW = NWOf<WideCfg<D, CAUSAL>>::v;
-  constexpr int BR = 32 * WideCfg<D, CAUSAL>::QB * NW;
+  constexpr int NW = NWOf<WideCfg<D, CAUSAL, LONG>>::v;
+  constexpr int BR = 32 * WideCfg<D, CAUSAL, LONG>::QB * NW;
   FwdParams q = p;
   q.nq = (p.N + BR - 1) / BR;
   const unsigned grid = (unsigned)(q.nq * p.BH);
-  hipLaunchKernelGGL((fwd_wide<T, D, CAUSAL>), dim3(grid), dim3(64 * NW), 0, stream, q);
+  hipLaunchKernelGGL((fwd_wide<T, D, CAUSAL, LONG>), dim3(grid), dim3(64 * NW), 0, stream, q);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_wide_t(const FwdParams& p, int d, int causal, hipStream_t s) {
+hipError_t launch_wide_t(const FwdParams& p, int d, int causal, int long_causal, hipStream_t s) {
   switch (d) {
     case 64:  return causal ? launch_wide<T, 64, true>(p, s) : launch_wide<T, 64, false>(p, s);
-    case 128: return causal ? launch_wide<T, 128, true>(p, s) : launch_wide<T, 128, false>(p, s);
+    case 128:
+      if (causal && long_causal) return launch_wide<T, 128, true, true>(p, s);
+      return causal ? launch_wide<T, 128, true>(p, s) : launch_wide<T, 128, false>(p, s);
     case 256: return causal ? launch_wide<T, 256, true>(p, s) : launch_wide<T, 256, false>(p, s);
   }
   return hipErrorInvalidValue;
@@ -509,12 +519,17 @@ static int blocks_per_cu(int d) {
 int wide_rows_per_block(int d, int causal) {
   return causal ? rows_per_block<true>(d) : rows_per_block<false>(d);
 }
+int wide_long_causal_rows(int d) {
+  return d == 128 ? 32 * NWOf<WideCfg<128, true, true>>::v * WideCfg<128, true, true>::QB : 0;
+}
 int wide_blocks_per_cu(int d, int causal) {
   return causal ? blocks_per_cu<true>(d) : blocks_per_cu<false>(d);
 }
 
-hipError_t launch_fwd_wide(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s) {
-  return is_bf16 ? launch_wide_t<__bf16>(p, d, causal, s) : launch_wide_t<_Float16>(p, d, causal, s);
+hipError_t launch_fwd_wide(const FwdParams& p, int d, int causal, int long_causal, int is_bf16,
+                           hipStream_t s) {
+  return is_bf16 ? launch_wide_t<__bf16>(p, d, causal, long_causal, s)
+                 : launch_wide_t<_Float16>(p, d, causal, long_causal, s);
 }
 
 

@@ -119,11 +119,15 @@ struct QuantParams {
 // fp16 / bf16 inputs, MFMA path.  d in {64, 128, 256}.
 hipError_t launch_fwd_half(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
 // fp16 / bf16 with 32 or 64 query rows per wave and one wave of each
-// workgroup per SIMD (fa_fwd_wide.hip).  d in {64, 128, 256}.
-hipError_t launch_fwd_wide(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
-// Query rows per workgroup and workgroups per CU of that kernel.
+// workgroup per SIMD (fa_fwd_wide.hip).  d in {64, 128, 256}; long_causal
+// (d = 128, causal) selects the configuration for many query tiles.
+hipError_t launch_fwd_wide(const FwdParams& p, int d, int causal, int long_causal, int is_bf16,
+                           hipStream_t s);
+// Query rows per workgroup and workgroups per CU of that kernel; rows per
+// workgroup of the long-causal configuration (0 where there is none).
 int wide_rows_per_block(int d, int causal);
 int wide_blocks_per_cu(int d, int causal);
+int wide_long_causal_rows(int d);
 // fp32 inputs (v_mfma_f32_32x32x2f32).  d in {64, 128, 256}.
 hipError_t launch_fwd_f32(const FwdParams& p, int d, int causal, hipStream_t s);
 // e4m3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4).  d = 128.

@@ -60,3 +60,10 @@ def test_gqa_equals_repeated_kv():
     o2, l2 = fa.attention(q, k[:, idx].contiguous(), v[:, idx].contiguous(), False, 0.088)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gqa_long_causal_configuration():
+    # 2 x 512 causal 512-row tiles at d = 128: the long-causal configuration,
+    # with four query heads per K/V head
+    _say("case gqa long-causal bf16 d=128 B=2 H=256 Hkv=64 N=600")
+    _case("bf16", 128, 1, 2, 256, 64, 600, seed=91)

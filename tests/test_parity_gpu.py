@@ -78,6 +78,20 @@ def test_many_heads_causal_every_element(dtype, d, BH, N):
     check(o, lse, o_ref, lse_ref, dtype, f"{dtype} BH={BH} N={N} causal")
 
 
+# Causal d = 128 launches with at least two rounds of 512-row workgroups (one
+# per CU, 256 CUs) take the long-causal configuration of the wide kernel (64
+# rows per wave, ping-pong halves); ragged sequence lengths, every element.
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("BH,N", [(512, 600), (256, 1030)])
+def test_long_causal_configuration_every_element(dtype, BH, N):
+    _say(f"case long-causal dtype={dtype} d=128 BH={BH} N={N}")
+    q, k, v = inputs.random_inputs(1, BH, N, 128, dtype, seed=BH + 7 * N)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    o, lse = run_gpu(q, k, v, 1, scale)
+    o_ref, lse_ref = oracle.attention(widen(q), widen(k), widen(v), 1, scale)
+    check(o, lse, o_ref, lse_ref, dtype, f"{dtype} BH={BH} N={N} causal")
+
+
 def _sample_rows(B, H, N, seed, per_head=24, heads=6):
     rng = np.random.default_rng(seed)
     hs = sorted(set([0, B * H - 1] + list(rng.integers(0, B * H, heads - 2))))
