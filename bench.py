@@ -112,7 +112,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); "
               "every (batch, head) is independent, so N GPUs would each run B*H/N heads "
               "with no communication — see the sharding paragraph of the design notes.",
               file=sys.stderr)

@@ -107,7 +107,7 @@ def _sample_rows(B, H, N, seed, per_head=24, heads=6):
 FULL = [w for w in inputs.WORKLOADS if w.dtype != "e4m3"]
 
 
-@pytest.mark.parametrize("w", FULL, ids=lambda w: f"cfg{w.config_id}.{w.case_id}")
+@pytest.mark.parametrize("w", FULL, ids=lambda w: f"{w.name}.{w.case_id}")
 def test_workload_full_size_sampled_rows(w):
     _say(f"case workload {w.label()}")
     q, k, v = inputs.workload_inputs(w)
