@@ -74,13 +74,21 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // a head share that XCD's L2 for K and V.  Without masking, an XCD runs its
 // heads one after another (the tiles of a head stream the same K/V tiles at
 // about the same time); with causal masking it goes tile-major, heaviest
-// (last) query tiles of every head first, for load balance.
+// (last) query tiles of every head first, for load balance.  snake > 0 (the
+// workgroups per CU of the launch): the first snake passes over an XCD's 32
+// CUs, which fill the CUs' slots, alternate direction, so that a CU that
+// receives one of the heaviest tiles in the first pass receives one of the
+// lighter tiles of the second (2% on the 2048-token causal training shape
+// at three workgroups per CU).
 __device__ __forceinline__ void decode_block(int bid, int BH, int nq, bool causal,
-                                             int& bh, int& qt) {
+                                             int& bh, int& qt, int snake = 0) {
   int t;
   if ((BH & 7) == 0) {
-    const int hx = BH >> 3, xcd = bid & 7, loc = bid >> 3;
+    const int hx = BH >> 3, xcd = bid & 7;
+    int loc = bid >> 3;
     if (causal) {  // tile-major: heavy tiles of every head first
+      const int pass = loc >> 5;  // complete passes only, so the map stays a bijection
+      if ((pass & 1) && pass < snake && (pass + 1) * 32 <= nq * hx) loc = (pass << 5) + 31 - (loc & 31);
       t = loc / hx;
       bh = xcd * hx + loc % hx;
     } else {       // head-major: a head's tiles run together and share K/V in L2

@@ -130,7 +130,7 @@ void fwd_wide(FwdParams p) {
   const int ql = lane & 31, g = lane >> 5;
   const int N = p.N;
   int bh, qt;
-  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt);
+  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt, (CAUSAL && NW == 4) ? Cfg::OCC : 0);
 
   const size_t head = (size_t)bh * N * D;
   const T* __restrict__ qh = (const T*)p.q + head;
