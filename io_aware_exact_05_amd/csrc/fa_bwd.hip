@@ -225,7 +225,8 @@ void bwd_dq(BwdParams p) {
   const int ql = lane & 31, g = lane >> 5;
   const int N = p.N;
   int bh, qt;
-  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt);
+  // causal: the first passes over an XCD's CUs alternate direction (workgroups per CU)
+  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt, BwdCfg<D>::OCC_DQ * 4 / kBwdNW);
   const size_t head = (size_t)bh * N * D;
   const size_t kvhead = (size_t)kv_head_of(p.H, p.Hkv, bh) * N * D;
   const T* __restrict__ kh = (const T*)p.k + kvhead;
@@ -360,7 +361,7 @@ void bwd_dkdv(BwdParams p) {
   const int N = p.N;
   const int BHkv = p.BH / (p.H / p.Hkv), grp = p.H / p.Hkv;
   int kvbh, t;
-  decode_block(blockIdx.x, BHkv, p.nq, CAUSAL, kvbh, t);
+  decode_block(blockIdx.x, BHkv, p.nq, CAUSAL, kvbh, t, BwdCfg<D>::OCC_KV * 4 / kBwdNW);
   const int kblk = CAUSAL ? p.nq - 1 - t : t;  // causal: low key blocks (most work) first
   const int b = kvbh / p.Hkv, gk = kvbh % p.Hkv;
   const int qh0 = b * p.H + gk * grp;          // first query head of the group

@@ -79,7 +79,8 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // CUs, which fill the CUs' slots, alternate direction, so that a CU that
 // receives one of the heaviest tiles in the first pass receives one of the
 // lighter tiles of the second (2% on the 2048-token causal training shape
-// at three workgroups per CU).
+// at three workgroups per CU, 7% for its backward at two, 3-4% for fp8 at
+// d = 64 and 256).
 __device__ __forceinline__ void decode_block(int bid, int BH, int nq, bool causal,
                                              int& bh, int& qt, int snake = 0) {
   int t;

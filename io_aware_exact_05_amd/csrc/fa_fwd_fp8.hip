@@ -125,7 +125,8 @@ void fwd_fp8(Fp8Params p) {
   const int ql = lane & 31, g = lane >> 5;
   const int N = p.N;
   int bh, qt;
-  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt);
+  // causal: the first passes over an XCD's CUs alternate direction (workgroups per CU)
+  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt, FA_FP8_OCC * 4 / NW);
   const size_t head = (size_t)bh * N * D;
   const uint8_t* __restrict__ qh = p.q + head;
   const uint8_t* __restrict__ kh = p.k + head;
