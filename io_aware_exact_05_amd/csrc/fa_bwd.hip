@@ -47,7 +47,9 @@ constexpr int kBwdNW = 4;  // waves per workgroup (32 rows or keys each)
 // bwd_dq streams 32-key tiles through a 4-stage ring (the same 64 KiB of LDS
 // as 64-key tiles in 2 stages): 5-7% faster on 2048-token heads, equal on
 // 8192-token heads; bwd_dkdv takes 32-query tiles with V in LDS at two waves
-// per SIMD (see bwd_dkdv).  The FA_BWD_* macros exist for tuning builds only.
+// per SIMD (see bwd_dkdv).  At d = 64 bwd_dq fits three waves per SIMD (138
+// registers): up to 10% over two (bwd_dkdv at three, with 32-query tiles, did
+// not add to it).  The FA_BWD_* macros exist for tuning builds only.
 #ifndef FA_BWD_D64_BC
 #define FA_BWD_D64_BC 64
 #endif
@@ -74,7 +76,7 @@ constexpr int kBwdNW = 4;  // waves per workgroup (32 rows or keys each)
 #endif
 template <int D> struct BwdCfg;
 template <> struct BwdCfg<64> {
-  static constexpr int BC = FA_BWD_D64_BC, BQ = FA_BWD_D64_BQ, OCC_DQ = 2, OCC_KV = 2;
+  static constexpr int BC = FA_BWD_D64_BC, BQ = FA_BWD_D64_BQ, OCC_DQ = 3, OCC_KV = 2;
   static constexpr int ST_DQ = FA_BWD_D64_STDQ, ST_KV = FA_BWD_D64_STKV;
 };
 template <> struct BwdCfg<128> {
