@@ -82,9 +82,9 @@ def kernel_name(w) -> str:
     if w.dtype == "f32":
         return "fwd_f32"
     # rows per workgroup and workgroups per CU of the one-wave-per-SIMD kernel
-    if w.d == 128 and w.causal and (w.N + 511) // 512 * w.B * w.H >= 2 * 256:
+    if w.d in (64, 128) and w.causal and (w.N + 511) // 512 * w.B * w.H >= 2 * 256:
         return "fwd_wide (long causal)"
-    rows, per_cu = {(64, 0): (512, 1), (64, 1): (512, 1), (128, 0): (512, 1), (128, 1): (128, 3),
+    rows, per_cu = {(64, 0): (512, 1), (64, 1): (128, 3), (128, 0): (512, 1), (128, 1): (128, 3),
                     (256, 0): (256, 1), (256, 1): (256, 1)}.get((w.d, w.causal), (0, 0))
     if rows and (not w.causal or (w.N + rows - 1) // rows * w.B * w.H > per_cu * 256):
         return "fwd_wide"

@@ -79,9 +79,20 @@ constexpr bool swz_step4_is_xor1() {
 //           halves (+1-2% over two 4-wave workgroups);
 //   d = 64: 64 rows per wave and 64-key tiles (the state is small), one
 //           8-wave workgroup per CU with ping-pong halves (+10-12% over the
-//           32-row 8-wave kernel).
+//           32-row 8-wave kernel); causal launches with fewer than two rounds
+//           of those 512-row workgroups take 32 rows per wave at three waves
+//           per SIMD instead (15-18% over the 8-wave 32-row kernel they used
+//           to fall back to at 1024-2048 tokens).
 template <int D, bool CAUSAL, bool LONG = false> struct WideCfg;
-template <bool C> struct WideCfg<64, C> {
+template <> struct WideCfg<64, false> {
+  static constexpr int QB = 2, BC = 64, ST = 3, OCC = 2, NW = 8;
+  static constexpr bool XK = false, XV = false;
+};
+template <> struct WideCfg<64, true> {
+  static constexpr int QB = 1, BC = 64, ST = 3, OCC = 3;
+  static constexpr bool XK = false, XV = false;
+};
+template <> struct WideCfg<64, true, true> {
   static constexpr int QB = 2, BC = 64, ST = 3, OCC = 2, NW = 8;
   static constexpr bool XK = false, XV = false;
 };
@@ -478,7 +489,9 @@ hipError_t launch_wide(const FwdParams& p, hipStream_t stream) {
 template <typename T>
 hipError_t launch_wide_t(const FwdParams& p, int d, int causal, int long_causal, hipStream_t s) {
   switch (d) {
-    case 64:  return causal ? launch_wide<T, 64, true>(p, s) : launch_wide<T, 64, false>(p, s);
+    case 64:
+      if (causal && long_causal) return launch_wide<T, 64, true, true>(p, s);
+      return causal ? launch_wide<T, 64, true>(p, s) : launch_wide<T, 64, false>(p, s);
     case 128:
       if (causal && long_causal) return launch_wide<T, 128, true, true>(p, s);
       return causal ? launch_wide<T, 128, true>(p, s) : launch_wide<T, 128, false>(p, s);
@@ -520,7 +533,11 @@ int wide_rows_per_block(int d, int causal) {
   return causal ? rows_per_block<true>(d) : rows_per_block<false>(d);
 }
 int wide_long_causal_rows(int d) {
-  return d == 128 ? 32 * NWOf<WideCfg<128, true, true>>::v * WideCfg<128, true, true>::QB : 0;
+  switch (d) {
+    case 64: return 32 * NWOf<WideCfg<64, true, true>>::v * WideCfg<64, true, true>::QB;
+    case 128: return 32 * NWOf<WideCfg<128, true, true>>::v * WideCfg<128, true, true>::QB;
+  }
+  return 0;
 }
 int wide_blocks_per_cu(int d, int causal) {
   return causal ? blocks_per_cu<true>(d) : blocks_per_cu<false>(d);

@@ -120,7 +120,7 @@ struct QuantParams {
 hipError_t launch_fwd_half(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
 // fp16 / bf16 with 32 or 64 query rows per wave and one wave of each
 // workgroup per SIMD (fa_fwd_wide.hip).  d in {64, 128, 256}; long_causal
-// (d = 128, causal) selects the configuration for many query tiles.
+// (d = 64 or 128, causal) selects the configuration for many query tiles.
 hipError_t launch_fwd_wide(const FwdParams& p, int d, int causal, int long_causal, int is_bf16,
                            hipStream_t s);
 // Query rows per workgroup and workgroups per CU of that kernel; rows per
