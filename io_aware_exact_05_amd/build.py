@@ -15,12 +15,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["api.cpp", "fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip",
+SOURCES = ["api.cpp", "fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_pipe.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip",
            "fa_quant.hip", "fa_bwd.hip", "fa_decode.hip"]
-# Extra flags per source.  fa_fwd_wide.hip keeps its MFMA accumulators in
-# VGPRs (VGPR form): its registers then fit two waves per SIMD with no copies
-# between the VGPR and AGPR files.
-SOURCE_FLAGS = {"fa_fwd_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Extra flags per source.  fa_fwd_wide.hip and fa_fwd_pipe.hip keep their
+# MFMA accumulators in VGPRs (VGPR form): their registers then fit two waves
+# per SIMD with no copies between the VGPR and AGPR files.  fa_fwd_pipe.hip
+# also assumes no NaN operands, which lets a row maximum be v_max3_f32 chains
+# without canonicalising every MFMA result first.
+SOURCE_FLAGS = {"fa_fwd_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "fa_fwd_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled: hipcc -O3 would otherwise form

@@ -50,6 +50,29 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
                : "memory", "m0");
 }
 
+// Raw buffer resource over [base, base + bytes) (stride 0; data format 32 bit,
+// the value the gfx9 family expects for untyped buffer loads).
+// The base address and size go through readfirstlane: the resource must
+// live in scalar registers, and this states that they are wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// 16-byte buffer -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane i's
+// bytes land at LDS address lds_addr + 16 i.  An offset past the resource's
+// size reads zeros instead of memory.  Inline assembly for the same reason
+// as dma16: the caller does its own vmcnt accounting.
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kMInit = -1.0e30f;  // finite start of the running max
 constexpr float kLazy = 8.0f;       // log2 headroom before the running max moves

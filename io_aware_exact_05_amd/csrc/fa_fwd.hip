@@ -433,8 +433,13 @@ static int wide_kind(const FwdParams& p, int d, int causal) {
   return grid > (long long)wide_blocks_per_cu(d, causal) * cus ? 1 : 0;
 }
 
+#ifndef FA_PIPE_D128
+#define FA_PIPE_D128 1
+#endif
+
 template <typename T>
 static hipError_t launch_t(const FwdParams& p, int d, int causal, hipStream_t s) {
+  if (FA_PIPE_D128 && d == 128) return launch_fwd_pipe(p, d, causal, std::is_same<T, __bf16>::value, s);
   const int kind = wide_kind(p, d, causal);
   if (kind) return launch_fwd_wide(p, d, causal, kind == 2, std::is_same<T, __bf16>::value, s);
   switch (d) {

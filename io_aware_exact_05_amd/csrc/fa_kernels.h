@@ -128,6 +128,9 @@ hipError_t launch_fwd_wide(const FwdParams& p, int d, int causal, int long_causa
 int wide_rows_per_block(int d, int causal);
 int wide_blocks_per_cu(int d, int causal);
 int wide_long_causal_rows(int d);
+// fp16 / bf16, d = 128, softmax software-pipelined against the matrix
+// products inside each wave (fa_fwd_pipe.hip).
+hipError_t launch_fwd_pipe(const FwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
 // fp32 inputs (v_mfma_f32_32x32x2f32).  d in {64, 128, 256}.
 hipError_t launch_fwd_f32(const FwdParams& p, int d, int causal, hipStream_t s);
 // e4m3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4).  d = 128.
