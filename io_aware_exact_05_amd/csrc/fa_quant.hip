@@ -29,11 +29,12 @@
 #include <stdint.h>
 
 #include "fa_kernels.h"
+#include "fa_quant_index.h"
 
 namespace fa {
 namespace {
 
-constexpr int kBlockRows = 128;
+using qidx::kBlockRows;
 
 // 16-byte buffer -> LDS copy per lane (lane i's bytes land at lds_addr + 16 i;
 // offsets past the resource read zeros); the caller waits on vmcnt.
@@ -46,14 +47,15 @@ __device__ __forceinline__ void q_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 
 template <int D, bool ROT>
 __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
-  constexpr int E = D / 2;  // elements per thread (half a row)
-  constexpr bool STAGE = D <= 128;  // rows staged through LDS, 64 at a time
-  constexpr int RB = D * 4, CPR = RB / 16, HC = CPR / 2;  // row bytes, chunks per row, per half
+  using G = qidx::Geo<D, ROT>;
+  constexpr int E = G::E;  // elements per thread (half a row)
+  constexpr bool STAGE = G::STAGE;  // rows staged through LDS
+  constexpr int RB = G::RB, HC = G::HC;  // row bytes, chunks per half row
   // rows per staging pass: two passes of 64 rows with the rotation (32 KiB
   // at d = 128, so that more workgroups share a CU while they transform),
   // one pass of 128 without (measured: each is the faster choice there)
-  constexpr int NPASS = ROT ? 2 : 1, SR = kBlockRows / NPASS;
-  __shared__ __attribute__((aligned(1024))) char tile[STAGE ? SR * RB : 16];
+  constexpr int NPASS = G::NPASS, SR = G::SR;
+  __shared__ __attribute__((aligned(1024))) char tile[G::TILE_BYTES];
   const int t = threadIdx.x, r = t >> 1, hf = t & 1;
   const int bh = blockIdx.x / p.nblk, blk = blockIdx.x % p.nblk;
   const int row = blk * kBlockRows + r;
@@ -71,29 +73,27 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
     const uint64_t a = (uint64_t)(uintptr_t)(p.x + blk_elem);
     const uint32_t a_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t a_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    void* ub = (void*)(uintptr_t)(((uint64_t)a_hi << 32) | (uint64_t)a_lo);
+    void* ub = (void*)(uintptr_t)qidx::join_words(a_lo, a_hi);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         ub, 0, (int)__builtin_amdgcn_readfirstlane((uint32_t)(rows_left * RB)), 0x00020000);
     const int w = t >> 6, lane = t & 63;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)tile;
-    constexpr int NI = SR * CPR / 256;  // copies per thread and pass
+    constexpr int NI = G::NI;  // copies per thread and pass
     // with two passes, waves 0-1 take their rows from the first and waves
     // 2-3 from the second
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       if (ps == 1) __syncthreads();  // the first pass's rows have been read
 #pragma unroll
-      for (int u = 0; u < NI; ++u) {
-        const int sl = (u * 4 + w) * 64 + lane, rr = sl / CPR, pos = sl % CPR;
-        q_dma16(rs, (uint32_t)((ps * SR + rr) * RB + ((pos ^ (rr % HC)) << 4)), lds0 + (u * 4 + w) * 1024);
-      }
+      for (int u = 0; u < NI; ++u)
+        q_dma16(rs, qidx::dma_src<D, ROT>(ps, u, w, lane), lds0 + qidx::dma_dst<D, ROT>(u, w));
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (r / SR == ps) {
         const int lr = r - ps * SR;
 #pragma unroll
         for (int k = 0; k < HC; ++k) {
-          const float4 v = *(const float4*)(tile + lr * RB + ((hf * HC + (k ^ (lr % HC))) << 4));
+          const float4 v = *(const float4*)(tile + qidx::stage_read<D, ROT>(lr, hf, k));
           x[4 * k] = v.x;
           x[4 * k + 1] = v.y;
           x[4 * k + 2] = v.z;
@@ -184,11 +184,11 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
   if constexpr (STAGE) {
     // codes row-major in LDS (D bytes per row; the 16-byte chunks of a row
     // XOR-swizzled by row), then 16-byte stores of whole rows
-    constexpr int CR = D / 16, HCR = CR / 2;  // code chunks per row and per half
+    constexpr int CR = G::CR;  // code chunks per row
     __syncthreads();  // every thread has read its fp32 half row
 #pragma unroll
     for (int i = 0; i < E / 16; ++i)
-      *(uint4*)(tile + r * D + ((hf * HCR + (i ^ (r % HCR))) << 4)) =
+      *(uint4*)(tile + qidx::code_write<D>(r, hf, i)) =
           make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
     __syncthreads();
     const int rows_left = min(kBlockRows, p.N - blk * kBlockRows);
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantParams p) {
 #pragma unroll
     for (int u = 0; u < kBlockRows * CR / 256; ++u) {
       const int sl = u * 256 + t, rr = sl / CR, c = sl % CR;
-      const uint4 val = *(const uint4*)(tile + rr * D + (((c & ~(HCR - 1)) | ((c ^ (rr % HCR)) & (HCR - 1))) << 4));
+      const uint4 val = *(const uint4*)(tile + qidx::code_read<D>(rr, c));
       if (rr < rows_left) *(uint4*)(dst + (size_t)rr * D + c * 16) = val;
     }
   } else if (valid) {
