@@ -5,7 +5,7 @@ for bit without rotation; within one code step (and descales within 2e-6)
 with the randomised Hadamard rotation, whose fp32 butterflies round
 differently from the oracle's fp64 matrix product.
 Attention, end to end: fp8 output against the fp64 oracle run on the
-UNQUANTISED fp32 inputs, gated on the sampled-rows relative RMSE <= 5e-2.
+UNQUANTISED fp32 inputs, gated on the whole-tensor relative RMSE <= 5e-2.
 Attention kernel alone: the oracle runs on exactly the values the codes
 stand for, and every output element must lie within a bound derived from
 the kernel's arithmetic (see _fp8_kernel_bounds).
@@ -25,11 +25,6 @@ from oracle import quant_oracle as qo
 pytestmark = pytest.mark.gpu
 
 REL_RMSE_GATE = 5e-2
-# End-to-end bound for the d = 64, d = 256 and causal variants of the fp8
-# workload, which the stated gate does not cover.  At d = 64 the rotation
-# spreads an outlier over 64 columns instead of 128, so the block amax (and
-# with it the code step) stays larger: 0.058 measured with rotation.
-VARIANT_REL_RMSE = 1e-1
 
 
 def _fa():
@@ -198,47 +193,76 @@ def test_fp8_attention_exactly_representable_inputs(d, causal):
     assert ro <= 1.0 and rl <= 1.0
 
 
-def _sample_rows(B, H, N, seed, per_head=24, heads=6):
-    rng = np.random.default_rng(seed)
-    hs = sorted(set([0, B * H - 1] + list(rng.integers(0, B * H, heads - 2))))
-    rows = []
-    for bh in hs:
-        rs = set([0, 1, 127, 128, N // 2, N - 1]) | set(int(x) for x in rng.integers(0, N, per_head))
-        rows += [bh * N + r for r in sorted(rs)]
-    return np.array(rows, np.int64)
-
-
 @pytest.mark.parametrize("case", [0, 1, 2, 3])
 def test_fp8_workload_rotation_and_without(case):
-    # case 0 is the fp8 configuration; 1-3 its d = 64, d = 256 and causal variants
+    """Whole-tensor relative RMSE of the fp8 workload and its variants
+    against the fp64 oracle on the unquantised fp32 inputs, with and without
+    the rotation of Q and K.  Case 0 is the fp8 configuration (d = 128,
+    non-causal); 1-3 its d = 64, d = 256 and causal variants.  The 5e-2 gate
+    holds for cases 0, 2 and 3; at d = 64 the rotation spreads an outlier
+    over only 64 columns and the end-to-end error stays above it (reported,
+    not gated; the kernel arithmetic of that variant is gated element by
+    element in test_fp8_kernel_on_oracle_quantised_inputs)."""
     w = inputs.workload(5, case)
     _say(f"case fp8 workload {w.label()}")
     fa = _fa()
     q, k, v = inputs.workload_inputs(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     signs = inputs.rotation_signs(w.d, seed=0).cuda()
-    rows = _sample_rows(w.B, w.H, w.N, seed=55)
-    o_ref, lse_ref = oracle.attention_rows(widen(q), widen(k), widen(v), w.causal, w.scale, rows)
+    o_ref, lse_ref = oracle.attention(widen(q), widen(k), widen(v), w.causal, w.scale)
     errs = {}
     for rot in (True, False):
         o, lse = fa.attention_fp8(qd, kd, vd, bool(w.causal), w.scale, rot, signs if rot else None)
         torch.cuda.synchronize()
         assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-        o_s = widen(o.reshape(-1, w.d)[torch.from_numpy(rows).cuda()].cpu())
-        lse_s = widen(lse.reshape(-1)[torch.from_numpy(rows).cuda()].cpu())
-        errs[rot] = (_rel_rmse(o_s, o_ref), float(np.abs(lse_s - lse_ref).max()))
+        errs[rot] = (_rel_rmse(widen(o.cpu()), o_ref), float(np.abs(widen(lse.cpu()) - lse_ref).max()))
     _say(f"  rel-RMSE with rotation {errs[True][0]:.4f} (max|dLSE| {errs[True][1]:.4f}); "
          f"without {errs[False][0]:.4f} (max|dLSE| {errs[False][1]:.4f}); "
          f"ratio {errs[False][0] / errs[True][0]:.2f}")
-    if case == 0:  # the fp8 configuration: the stated 5e-2 gate
+    assert errs[True][0] <= errs[False][0]  # the rotation never makes it worse
+    if w.d != 64:
         assert errs[True][0] <= REL_RMSE_GATE
-    else:
-        # variants of it: their kernel arithmetic is gated element by element
-        # above (test_fp8_kernel_on_oracle_quantised_inputs); end to end the
-        # quantisation error is reported, bounded loosely, and the rotation
-        # must not make it worse
-        assert errs[True][0] <= VARIANT_REL_RMSE
-        assert errs[True][0] <= errs[False][0]
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_mfma_dot_product_error(d):
+    """The premise of the kernel-alone fp8 bound: a dot product of e4m3
+    values on the scaled fp8 MFMA lies within 2^-10 of the sum of the terms'
+    magnitudes of the exact value.  With one key per head the kernel's only
+    score is S = q . k (descales 1), P = 1, l = 1, so LSE = scale S up to
+    three fp32 roundings; 2048 heads of random finite codes, and 2048 of
+    codes of quantised normal data, through the C ABI."""
+    fa = _fa()
+    rng = np.random.default_rng(9000 + d)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    for kind in ("uniform codes", "quantised normals"):
+        BH = 2048
+        if kind == "uniform codes":
+            q8 = rng.choice(finite, size=(1, BH, 1, d))
+            k8 = rng.choice(finite, size=(1, BH, 1, d))
+        else:
+            q8 = qo.e4m3_encode(rng.standard_normal((1, BH, 1, d)) * 64.0)
+            k8 = qo.e4m3_encode(rng.standard_normal((1, BH, 1, d)) * 64.0)
+        terms = qo.e4m3_decode(q8).astype(np.float64) * qo.e4m3_decode(k8).astype(np.float64)
+        exact = terms.sum(-1)[..., 0]
+        mag = np.abs(terms).sum(-1)[..., 0]
+        scale = 2.0 ** -12
+        one = torch.ones((1, BH, 1), dtype=torch.float32, device="cuda")
+        o = torch.empty((1, BH, 1, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((1, BH, 1), dtype=torch.float32, device="cuda")
+        tq = torch.from_numpy(np.ascontiguousarray(q8)).cuda()
+        tk = torch.from_numpy(np.ascontiguousarray(k8)).cuda()
+        tv = torch.zeros_like(tq)
+        fa.fa_fwd_fp8(tq, tk, tv, one, one, one, o, lse, False, scale)
+        torch.cuda.synchronize()
+        s_gpu = widen(lse.cpu())[..., 0] / scale
+        err = np.abs(s_gpu - exact)
+        bound = 2.0 ** -10 * mag + 4 * 2.0 ** -24 * np.abs(exact)
+        worst = float((err / np.maximum(bound, 1e-300)).max())
+        _say(f"  d={d} {kind}: max |S - exact| / (sum|terms|) = {float((err / np.maximum(mag, 1e-300)).max()):.3e}"
+             f"  (2^{np.log2(max(float((err / np.maximum(mag, 1e-300)).max()), 1e-30)):.1f}); worst/bound {worst:.3f}")
+        assert np.isfinite(s_gpu).all()
+        assert (err <= bound).all(), worst
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])

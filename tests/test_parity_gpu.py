@@ -2,8 +2,7 @@
 
 Small shapes compare every element and span several tiles plus a ragged tail;
 the full-size workloads run in the same launch configuration the benchmark
-times and compare sampled rows (first, last, tile-boundary and random rows of
-first, last and random heads), plus a finiteness check of every element.
+times and compare every element of O and the LSE with the full fp64 oracle.
 Gates: |O - O_ref| <= 1e-2 + half an output ulp of O_ref, |LSE - LSE_ref| <= 1e-3.
 """
 import math
@@ -59,13 +58,13 @@ def test_small_shapes_every_element(dtype, d, N, causal):
         assert st["o_max_abs"] < 1e-4 and st["lse_max_abs"] < 1e-4, st
 
 
-# Each head dimension has two kernels: causal launches whose grid fits in one
-# round of the wide kernel's workgroup slots (one 512-row workgroup per CU at
-# d = 64, three 128-row ones at d = 128, one 256-row one at d = 256) go to the 8-wave
-# 32-row kernel, all others to the former.  The small shapes above take the
-# first route for causal masking; these head counts push small, ragged causal
-# launches past 768 workgroups so the wide kernel is checked element by
-# element too.
+# Kernel routing: d = 128 always runs fwd_pipe (256-row workgroups).  At
+# d = 64 and 256, causal launches whose grid fits in one round of fwd_wide's
+# workgroup slots (one 512-row workgroup per CU at d = 64, one 256-row one at
+# d = 256) go to the 8-wave 32-row fwd_mfma16, all others to fwd_wide.  The
+# small shapes above take the fwd_mfma16 route for causal masking at d = 64
+# and 256; these head counts push small, ragged causal launches onto the
+# other kernels, element by element.
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("BH,N", [(800, 100), (400, 300), (260, 257)])
@@ -78,48 +77,36 @@ def test_many_heads_causal_every_element(dtype, d, BH, N):
     check(o, lse, o_ref, lse_ref, dtype, f"{dtype} BH={BH} N={N} causal")
 
 
-# Causal d = 128 launches with at least two rounds of 512-row workgroups (one
-# per CU, 256 CUs) take the long-causal configuration of the wide kernel (64
-# rows per wave, ping-pong halves); ragged sequence lengths, every element.
+# Causal launches with at least two rounds of 512-row workgroups (one per
+# CU, 256 CUs) take, at d = 64, the long-causal configuration of fwd_wide
+# (64 rows per wave, ping-pong halves); at d = 128 the same shapes run
+# fwd_pipe with many query tiles per head and diagonal tiles at every query
+# tile; ragged sequence lengths, every element.
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("BH,N", [(512, 600), (256, 1030)])
-def test_long_causal_configuration_every_element(dtype, BH, N):
-    _say(f"case long-causal dtype={dtype} d=128 BH={BH} N={N}")
-    q, k, v = inputs.random_inputs(1, BH, N, 128, dtype, seed=BH + 7 * N)
-    scale = float(np.float32(1 / math.sqrt(128)))
+def test_long_causal_configuration_every_element(dtype, d, BH, N):
+    _say(f"case long-causal dtype={dtype} d={d} BH={BH} N={N}")
+    q, k, v = inputs.random_inputs(1, BH, N, d, dtype, seed=BH + 7 * N + d)
+    scale = float(np.float32(1 / math.sqrt(d)))
     o, lse = run_gpu(q, k, v, 1, scale)
     o_ref, lse_ref = oracle.attention(widen(q), widen(k), widen(v), 1, scale)
     check(o, lse, o_ref, lse_ref, dtype, f"{dtype} BH={BH} N={N} causal")
-
-
-def _sample_rows(B, H, N, seed, per_head=24, heads=6):
-    rng = np.random.default_rng(seed)
-    hs = sorted(set([0, B * H - 1] + list(rng.integers(0, B * H, heads - 2))))
-    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, N // 2, N - 2, N - 1]
-    rows = []
-    for bh in hs:
-        rs = set(r for r in fixed if 0 <= r < N)
-        rs |= set(int(x) for x in rng.integers(0, N, per_head - len(rs)))
-        rows += [bh * N + r for r in sorted(rs)]
-    return np.array(rows, np.int64)
 
 
 FULL = [w for w in inputs.WORKLOADS if w.dtype != "e4m3"]
 
 
 @pytest.mark.parametrize("w", FULL, ids=lambda w: f"{w.name}.{w.case_id}")
-def test_workload_full_size_sampled_rows(w):
+def test_workload_full_size_every_element(w):
+    """Every element of O and the LSE of each full-size workload against the
+    full fp64 oracle (the result is exact up to rounding, "FlashAttention
+    (HI)", online-softmax section, so one gate holds for every element)."""
     _say(f"case workload {w.label()}")
     q, k, v = inputs.workload_inputs(w)
     o, lse = run_gpu(q, k, v, w.causal, w.scale)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    rows = _sample_rows(w.B, w.H, w.N, seed=w.config_id * 10 + w.case_id)
-    if w.N <= 128 and w.B * w.H == 1:
-        rows = np.arange(w.N)
-    o_ref, lse_ref = oracle.attention_rows(widen(q), widen(k), widen(v), w.causal, w.scale, rows)
-    o_s = o.reshape(-1, w.d)[torch.from_numpy(rows)]
-    lse_s = lse.reshape(-1)[torch.from_numpy(rows)]
-    st = check(o_s, lse_s, o_ref, lse_ref, w.dtype, w.label())
+    o_ref, lse_ref = oracle.attention(widen(q), widen(k), widen(v), w.causal, w.scale)
+    st = check(o, lse, o_ref, lse_ref, w.dtype, w.label())
     _say(f"  {w.label()}: {st}")
 
 
