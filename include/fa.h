@@ -16,8 +16,10 @@
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers owned by the caller.  The library allocates
- *     nothing, frees nothing and keeps no mutable global state, so calls are
- *     thread-safe; calls that write the same buffers concurrently race.
+ *     nothing and frees nothing; calls that write the same buffers
+ *     concurrently race.  The one piece of mutable global state is the static
+ *     scratch of fa_fwd_kvcache_noalloc (one per device); every other entry
+ *     point keeps none.
  *   - Tensors are contiguous, row-major: q, k, v, o are [B, H, N, d] (each
  *     (b, h) pair is one N x d matrix of the formula); lse is [B, H, N] fp32.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
@@ -50,7 +52,8 @@ typedef enum {
   FA_ERR_ALIGN = -5,   /* q/k/v/o not 16-byte or lse not 4-byte aligned  */
   FA_ERR_ARG = -6,     /* causal not 0/1, scale not finite, bad option   */
   FA_ERR_ALIAS = -7,   /* an output overlaps an input or another output  */
-  FA_ERR_LAUNCH = -8   /* the HIP runtime rejected the launch            */
+  FA_ERR_LAUNCH = -8,  /* the HIP runtime rejected the launch            */
+  FA_ERR_SCRATCH = -9  /* the shape needs more than the static scratch  */
 } fa_status;
 
 /*
@@ -165,6 +168,32 @@ int fa_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float* 
  * not cut, and for invalid shapes).
  */
 size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Hkv, int Nq, int Nkv, int d);
+
+/* Size of the static scratch of fa_fwd_kvcache_noalloc, per device. */
+#define FA_KVCACHE_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * fa_fwd_kvcache_noalloc — fa_fwd_kvcache for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the same kernels, arguments and results, but the
+ * workspace is the library's static scratch of FA_KVCACHE_SCRATCH_BYTES
+ * bytes (a device array each GPU holds until the process ends) instead of a
+ * caller buffer.  The caller still passes q, k, v, o and lse.
+ *   - The scratch is the current device's (hipGetDevice); `stream` must
+ *     belong to that device.  Its address is looked up on the first call on
+ *     each device; no call allocates or frees memory.
+ *   - Every call on one device uses the same scratch and leaves its partial
+ *     results there; nothing in it needs to start at zero.  Calls that
+ *     overlap in time on one device (other streams, other threads) race.
+ *   - Status: those of fa_fwd_kvcache, and FA_ERR_SCRATCH when
+ *     fa_fwd_kvcache_workspace_bytes(...) exceeds FA_KVCACHE_SCRATCH_BYTES
+ *     (the cache cut keeps rows x chunks <= 16320, so no valid shape with
+ *     d <= 256 does); FA_ERR_LAUNCH also when the scratch address cannot
+ *     be obtained.
+ */
+int fa_fwd_kvcache_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Hkv, int Nq, int Nkv, int d, int causal, float scale,
+                           int dtype, void* stream);
 
 /*
  * fa_fwd_fp8 — the same pass with OCP e4m3fn (finite-only, max 448) inputs,

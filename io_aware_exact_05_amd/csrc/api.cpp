@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiMajor = 1, kAbiMinor = 4;
+constexpr int kAbiMajor = 1, kAbiMinor = 5;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -80,6 +80,75 @@ DecPlan dec_plan(int B, int H, int Hkv, int Nq, int Nkv) {
   return d;
 }
 
+// Argument checks of the key/value-cache pass up to its cut (shared by
+// fa_fwd_kvcache and fa_fwd_kvcache_noalloc, in the order of the statuses).
+int kvcache_check(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                  int H, int Hkv, int Nq, int Nkv, int d, int causal, float scale, int dtype,
+                  DecPlan* pl) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || Nq < 1 || Nkv < Nq) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_SHAPE;
+  if ((uint64_t)Nkv * d > (uint64_t)INT32_MAX || (uint64_t)B * H > (uint64_t)INT32_MAX)
+    return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
+  *pl = dec_plan(B, H, Hkv, Nq, Nkv);
+  if ((uint64_t)B * Hkv * pl->nrb * pl->nsplit > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// Alignment and overlap of the pass's buffers; ws (need bytes) may be NULL.
+int kvcache_check_buffers(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* ws, size_t need, int B, int H, int Hkv, int Nq, int Nkv, int d) {
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      (ws && !aligned(ws, 16)))
+    return FA_ERR_ALIGN;
+  const uint64_t rows = (uint64_t)B * H * Nq, kv_rows = (uint64_t)B * Hkv * Nkv;
+  const uint64_t eb = (uint64_t)d * 2;
+  const Range in[3] = {range_of(q, rows * eb), range_of(k, kv_rows * eb), range_of(v, kv_rows * eb)};
+  const Range out[3] = {range_of(o, rows * eb), range_of(lse, rows * 4), range_of(ws, ws ? need : 0)};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(out[i], out[j])) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
+// Parameters and launch of the pass; ws holds the chunks' partial results
+// when the cut has more than one chunk.
+int kvcache_launch(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+                   const DecPlan& pl, int B, int H, int Hkv, int Nq, int Nkv, int d, int causal,
+                   float scale, int dtype, void* stream) {
+  const uint64_t rows = (uint64_t)B * H * Nq;
+  fa::DecodeParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.ws_o = pl.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
+  p.ws_lse = pl.nsplit > 1 ? p.ws_o + rows * pl.nsplit * (uint64_t)d : nullptr;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nkv = Nkv;
+  p.R = pl.R;
+  p.nrb = pl.nrb;
+  p.nsplit = pl.nsplit;
+  p.chunk = pl.chunk;
+  p.rows = rows;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  (void)hipGetLastError();
+  const hipError_t e = fa::launch_decode_half(p, d, causal, dtype == FA_BF16,
+                                              reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,6 +166,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_ARG: return "FA_ERR_ARG: invalid option (causal, scale or similar)";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: the shape needs more workspace than the static scratch";
   }
   return "unknown fa_status";
 }
@@ -223,55 +293,31 @@ size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Hkv, int Nq, int Nkv, in
 int fa_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float* lse,
                    void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nkv,
                    int d, int causal, float scale, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-  if (B < 1 || H < 1 || Nq < 1 || Nkv < Nq) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
-  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_SHAPE;
-  if ((uint64_t)Nkv * d > (uint64_t)INT32_MAX || (uint64_t)B * H > (uint64_t)INT32_MAX)
-    return FA_ERR_SHAPE;
-  if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  if (!std::isfinite(scale)) return FA_ERR_ARG;
-  const DecPlan pl = dec_plan(B, H, Hkv, Nq, Nkv);
-  if ((uint64_t)B * Hkv * pl.nrb * pl.nsplit > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  DecPlan pl{};
+  const int st = kvcache_check(q, k, v, o, lse, B, H, Hkv, Nq, Nkv, d, causal, scale, dtype, &pl);
+  if (st != FA_OK) return st;
   const size_t need = fa_fwd_kvcache_workspace_bytes(B, H, Hkv, Nq, Nkv, d);
   if (need > 0 && (!workspace || workspace_bytes < need)) return workspace ? FA_ERR_ARG : FA_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
-      (need > 0 && !aligned(workspace, 16)))
-    return FA_ERR_ALIGN;
-  const uint64_t rows = (uint64_t)B * H * Nq, kv_rows = (uint64_t)B * Hkv * Nkv;
-  const uint64_t eb = (uint64_t)d * 2;
-  const Range in[3] = {range_of(q, rows * eb), range_of(k, kv_rows * eb), range_of(v, kv_rows * eb)};
-  const Range out[3] = {range_of(o, rows * eb), range_of(lse, rows * 4), range_of(workspace, need)};
-  for (int i = 0; i < 3; ++i) {
-    for (const Range& r : in)
-      if (overlap(out[i], r)) return FA_ERR_ALIAS;
-    for (int j = i + 1; j < 3; ++j)
-      if (overlap(out[i], out[j])) return FA_ERR_ALIAS;
-  }
-  fa::DecodeParams p{};
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.lse = lse;
-  p.ws_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  p.ws_lse = need > 0 ? p.ws_o + rows * pl.nsplit * (uint64_t)d : nullptr;
-  p.B = B;
-  p.H = H;
-  p.Hkv = Hkv;
-  p.Nq = Nq;
-  p.Nkv = Nkv;
-  p.R = pl.R;
-  p.nrb = pl.nrb;
-  p.nsplit = pl.nsplit;
-  p.chunk = pl.chunk;
-  p.rows = rows;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-  (void)hipGetLastError();
-  const hipError_t e = fa::launch_decode_half(p, d, causal, dtype == FA_BF16,
-                                              reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  const int sb = kvcache_check_buffers(q, k, v, o, lse, need > 0 ? workspace : nullptr, need, B, H, Hkv,
+                                       Nq, Nkv, d);
+  if (sb != FA_OK) return sb;
+  return kvcache_launch(q, k, v, o, lse, need > 0 ? workspace : nullptr, pl, B, H, Hkv, Nq, Nkv, d,
+                        causal, scale, dtype, stream);
+}
+
+int fa_fwd_kvcache_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int Hkv, int Nq, int Nkv, int d, int causal, float scale, int dtype,
+                           void* stream) {
+  DecPlan pl{};
+  const int st = kvcache_check(q, k, v, o, lse, B, H, Hkv, Nq, Nkv, d, causal, scale, dtype, &pl);
+  if (st != FA_OK) return st;
+  const size_t need = fa_fwd_kvcache_workspace_bytes(B, H, Hkv, Nq, Nkv, d);
+  if (need > FA_KVCACHE_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  const int sb = kvcache_check_buffers(q, k, v, o, lse, nullptr, 0, B, H, Hkv, Nq, Nkv, d);
+  if (sb != FA_OK) return sb;
+  void* ws = nullptr;
+  if (need > 0 && (fa::decode_scratch(&ws) != hipSuccess || !ws)) return FA_ERR_LAUNCH;
+  return kvcache_launch(q, k, v, o, lse, ws, pl, B, H, Hkv, Nq, Nkv, d, causal, scale, dtype, stream);
 }
 
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale,

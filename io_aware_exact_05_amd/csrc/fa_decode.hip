@@ -29,6 +29,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
+#include "fa.h"
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -337,6 +340,36 @@ static hipError_t launch_dec_d(const DecodeParams& p, int d, int causal, hipStre
 
 hipError_t launch_decode_half(const DecodeParams& p, int d, int causal, int is_bf16, hipStream_t s) {
   return is_bf16 ? launch_dec_d<__bf16>(p, d, causal, s) : launch_dec_d<_Float16>(p, d, causal, s);
+}
+
+// Workspace of the passes that may not allocate (fa_fwd_kvcache_noalloc):
+// the partial results of the cache chunks.  Each device holds its own copy
+// from the code object's load until the process ends.  The partial kernel
+// writes every entry the merge kernel reads, so nothing needs clearing
+// between calls; calls that overlap on one device share it and race.
+static __device__ __align__(256) char scratch[FA_KVCACHE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device; the array's name is only a host-side stand-in
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

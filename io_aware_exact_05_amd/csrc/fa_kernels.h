@@ -139,6 +139,10 @@ hipError_t launch_fwd_fp8(const Fp8Params& p, int d, int causal, hipStream_t s);
 hipError_t launch_bwd_half(const BwdParams& p, int d, int causal, int is_bf16, hipStream_t s);
 // Attention over a key/value cache, fp16 / bf16, split over the cache.
 hipError_t launch_decode_half(const DecodeParams& p, int d, int causal, int is_bf16, hipStream_t s);
+// Device address, on the current device, of the library's static scratch of
+// FA_KVCACHE_SCRATCH_BYTES bytes that fa_fwd_kvcache_noalloc uses as its
+// workspace (fa_decode.hip); looked up once per device.
+hipError_t decode_scratch(void** ptr);
 // fp32 -> e4m3 block quantiser, optional randomised Hadamard rotation.
 hipError_t launch_quantize_e4m3(const QuantParams& p, int d, int rotate, hipStream_t s);
 

@@ -25,11 +25,15 @@ DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_B
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
                 -4: "FA_ERR_HEADDIM", -5: "FA_ERR_ALIGN", -6: "FA_ERR_ARG",
-                -7: "FA_ERR_ALIAS", -8: "FA_ERR_LAUNCH"}
+                -7: "FA_ERR_ALIAS", -8: "FA_ERR_LAUNCH", -9: "FA_ERR_SCRATCH"}
+
+# FA_KVCACHE_SCRATCH_BYTES: the static scratch of fa_fwd_kvcache_noalloc, per device
+KVCACHE_SCRATCH_BYTES = 16 << 20
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_bytes",
-           "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_fwd_fp8", "fa_quantize_e4m3",
+           "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache_noalloc",
+           "fa_fwd_fp8", "fa_quantize_e4m3",
            "fa_status_string", "fa_abi_version")
 
 
@@ -60,6 +64,8 @@ def _load():
     lib.fa_fwd_kvcache.restype = i
     lib.fa_fwd_kvcache_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_kvcache_workspace_bytes.restype = sz
+    lib.fa_fwd_kvcache_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_kvcache_noalloc.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_quantize_e4m3.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp]
@@ -246,9 +252,15 @@ def fa_fwd_kvcache_raw(q, k, v, o, lse, ws, ws_bytes, B, H, Hkv, Nq, Nkv, d, cau
                                    int(dtype), stream))
 
 
-def fa_fwd_kvcache(q, k, v, o, lse, workspace, causal: bool, scale: float, stream=None) -> None:
-    """q, o [B,H,Nq,d]; k, v [B,Hkv,Nkv,d]; lse [B,H,Nq] fp32; workspace a uint8 device tensor
-    of at least kvcache_workspace_bytes(...) bytes (or None when that is 0)."""
+def fa_fwd_kvcache_noalloc_raw(q, k, v, o, lse, B, H, Hkv, Nq, Nkv, d, causal, scale, dtype,
+                               stream=0) -> int:
+    """Direct call of fa_fwd_kvcache_noalloc with integer pointers; returns the status."""
+    return int(_lib.fa_fwd_kvcache_noalloc(q, k, v, o, lse, int(B), int(H), int(Hkv), int(Nq),
+                                           int(Nkv), int(d), int(causal), float(scale), int(dtype),
+                                           stream))
+
+
+def _kvcache_shapes(q, k, v, o, lse):
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
         _dev(name, t)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape:
@@ -261,6 +273,13 @@ def fa_fwd_kvcache(q, k, v, o, lse, workspace, causal: bool, scale: float, strea
         raise ValueError("q, k, v, o must share float16 or bfloat16")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq):
         raise ValueError("lse must be float32 of shape [B, H, Nq]")
+    return B, H, Hkv, Nq, Nkv, d
+
+
+def fa_fwd_kvcache(q, k, v, o, lse, workspace, causal: bool, scale: float, stream=None) -> None:
+    """q, o [B,H,Nq,d]; k, v [B,Hkv,Nkv,d]; lse [B,H,Nq] fp32; workspace a uint8 device tensor
+    of at least kvcache_workspace_bytes(...) bytes (or None when that is 0)."""
+    B, H, Hkv, Nq, Nkv, d = _kvcache_shapes(q, k, v, o, lse)
     wp, wb = 0, 0
     if workspace is not None:
         _dev("workspace", workspace)
@@ -269,6 +288,15 @@ def fa_fwd_kvcache(q, k, v, o, lse, workspace, causal: bool, scale: float, strea
                               lse.data_ptr(), wp or None, wb, B, H, Hkv, Nq, Nkv, d,
                               int(bool(causal)), scale, DTYPE_CODE[q.dtype],
                               _stream_handle(stream)))
+
+
+def fa_fwd_kvcache_noalloc(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """fa_fwd_kvcache with the library's static per-device scratch as the workspace: the call
+    allocates nothing.  Calls that overlap in time on one device race on that scratch."""
+    B, H, Hkv, Nq, Nkv, d = _kvcache_shapes(q, k, v, o, lse)
+    _check(fa_fwd_kvcache_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), B, H, Hkv, Nq, Nkv, d, int(bool(causal)),
+                                      scale, DTYPE_CODE[q.dtype], _stream_handle(stream)))
 
 
 def attention_kvcache(q, k, v, causal: bool = False, scale: float | None = None, stream=None):

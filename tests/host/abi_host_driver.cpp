@@ -41,6 +41,14 @@ hipError_t launch_decode_half(const DecodeParams& p, int, int, int, hipStream_t)
   return hipSuccess;
 }
 hipError_t launch_quantize_e4m3(const QuantParams&, int, int, hipStream_t) { ++g_calls; return hipSuccess; }
+// the static scratch of the no-allocation pass, at a fake 256-byte-aligned address
+constexpr uintptr_t kScratchAddr = uintptr_t(11) << 36;
+int g_scratch_lookups = 0;
+hipError_t decode_scratch(void** ptr) {
+  ++g_scratch_lookups;
+  *ptr = reinterpret_cast<void*>(kScratchAddr);
+  return hipSuccess;
+}
 }  // namespace fa
 
 namespace {
@@ -126,6 +134,51 @@ int main() {
   }
   expect(fa_fwd_kvcache(P(Q), P(K), P(V), P(O), F(L), nullptr, 0, 1, 4, 4, 9, 8, 128, 1, 0.1f, FA_BF16,
                         nullptr), FA_ERR_SHAPE, "kvcache Nq > Nkv");
+
+  // ---- fa_fwd_kvcache_noalloc: same cut, workspace = the static scratch ----
+  for (const auto& s : shapes) {
+    const int B = s[0], H = s[1], Hkv = s[2], Nq = s[3], Nkv = s[4];
+    const size_t wb = fa_fwd_kvcache_workspace_bytes(B, H, Hkv, Nq, Nkv, 256);
+    g_dec = fa::DecodeParams{};
+    const int before = fa::g_scratch_lookups;
+    expect(fa_fwd_kvcache_noalloc(P(Q), P(K), P(V), P(O), F(L), B, H, Hkv, Nq, Nkv, 256, 1, 0.1f, FA_F16,
+                                  nullptr), FA_OK, "noalloc ok");
+    const uintptr_t wso = reinterpret_cast<uintptr_t>(g_dec.ws_o), wsl = reinterpret_cast<uintptr_t>(g_dec.ws_lse);
+    if (wb) {
+      expect((int)(wso == fa::kScratchAddr), 1, "noalloc partial O in the scratch");
+      expect((int)(wsl + (uint64_t)B * H * Nq * g_dec.nsplit * 4 == fa::kScratchAddr + wb), 1,
+             "noalloc partial LSE ends the workspace");
+      expect(fa::g_scratch_lookups - before, 1, "noalloc looks the scratch up");
+    } else {
+      expect((int)(wso == 0 && wsl == 0), 1, "noalloc single chunk uses no workspace");
+      expect(fa::g_scratch_lookups - before, 0, "noalloc single chunk needs no scratch");
+    }
+  }
+  expect(fa_fwd_kvcache_noalloc(nullptr, P(K), P(V), P(O), F(L), 1, 4, 4, 1, 4096, 128, 0, 0.1f, FA_BF16,
+                                nullptr), FA_ERR_NULL, "noalloc null q");
+  expect(fa_fwd_kvcache_noalloc(P(Q), P(K), P(V), P(O), F(L), 1, 4, 4, 1, 4096, 96, 0, 0.1f, FA_BF16,
+                                nullptr), FA_ERR_HEADDIM, "noalloc d96");
+  expect(fa_fwd_kvcache_noalloc(P(Q), P(K), P(V), P(O), F(L), 1, 4, 4, 1, 4096, 128, 0, 0.1f, FA_F32,
+                                nullptr), FA_ERR_DTYPE, "noalloc f32");
+  expect(fa_fwd_kvcache_noalloc(P(Q), P(K), P(V), P(K), F(L), 1, 4, 4, 1, 4096, 128, 0, 0.1f, FA_BF16,
+                                nullptr), FA_ERR_ALIAS, "noalloc o on k");
+  expect(fa_fwd_kvcache_noalloc(P(Q + 8), P(K), P(V), P(O), F(L), 1, 4, 4, 1, 4096, 128, 0, 0.1f, FA_BF16,
+                                nullptr), FA_ERR_ALIGN, "noalloc misaligned q");
+  // The cut keeps (rows) x (chunks) <= 32 base ceil(256 / base) <= 16320 with
+  // base = B Hkv ceil(R / 32) < 256 (one chunk otherwise), so every shape with
+  // d <= 256 fits the scratch; the worst case is base = 255 with two chunks.
+  size_t worst = 0;
+  for (int base = 1; base <= 300; ++base)
+    for (int G : {1, 2, 4, 8, 32})
+      for (int Nq : {1, 3, 8, 31, 32}) {
+        const int R = G * Nq, nrb = (R + 31) / 32;
+        if (base % nrb) continue;
+        const int BHkv = base / nrb;
+        const size_t w = fa_fwd_kvcache_workspace_bytes(BHkv, G, 1, Nq, 1 << 20, 256);
+        if (w > worst) worst = w;
+      }
+  expect((int)(worst <= FA_KVCACHE_SCRATCH_BYTES), 1, "every cut fits the static scratch");
+  expect((int)(worst == (size_t)16320 * 257 * 4), 1, "worst cut is 16320 partial rows of d = 256");
 
   // ---- fp8 ----
   expect(fa_fwd_fp8(P(Q), P(K), P(V), F(WS), F(WS + 4096), F(WS + 8192), P(O), F(L), 2, 3, 300, 256, 1,

@@ -249,3 +249,33 @@ def test_kvcache_no_workspace_needed_accepts_null():
     # so check with an invalid dtype that validation reached the later checks
     a = _kv_args(Nkv=300, ws=0, ws_bytes=0, causal=5)
     assert fa.fa_fwd_kvcache_raw(**a) == -6
+
+
+# --------- the same pass with the library's static scratch as workspace ----------
+def _kvn_args(**kw):
+    a = _kv_args(**kw)
+    del a["ws"], a["ws_bytes"]
+    return a
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_kvcache_noalloc_null_pointer(which):
+    assert fa.fa_fwd_kvcache_noalloc_raw(**_kvn_args(**{which: 0})) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(Nq=3, Nkv=2), -2), (dict(Hkv=3), -2), (dict(d=96), -4),
+    (dict(dtype=fa.FA_F32), -3), (dict(causal=2), -6), (dict(scale=float("inf")), -6),
+    (dict(q=KC["q"] + 8), -5), (dict(lse=KC["lse"] + 2), -5),
+    (dict(o=KC["k"]), -7), (dict(lse=KC["o"]), -7),
+])
+def test_kvcache_noalloc_invalid_arguments(kw, code):
+    # validated like fa_fwd_kvcache, before any HIP call
+    assert fa.fa_fwd_kvcache_noalloc_raw(**_kvn_args(**kw)) == code
+
+
+def test_kvcache_scratch_covers_every_cut():
+    # the worst cut: 255 K/V-head row blocks of 32 rows, two chunks, d = 256
+    assert fa.kvcache_workspace_bytes(255, 32, 1, 1, 1 << 20, 256) == 16320 * 257 * 4
+    assert 16320 * 257 * 4 <= fa.KVCACHE_SCRATCH_BYTES
+    assert fa.status_string(-9).startswith("FA_ERR_SCRATCH")
