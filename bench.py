@@ -46,7 +46,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_d128_B4H16N2048_noncausal_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_exact_05_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_fwd_wide.hip", "fa_device.h", "fa_kernels.h")]
+                  for f in ("fa_fwd.hip", "fa_fwd_pipe.hip", "fa_device.h", "fa_kernels.h")]
 
 
 def kernel_source_sha() -> str:
@@ -81,6 +81,8 @@ def kernel_name(w) -> str:
         return "fwd_fp8"
     if w.dtype == "f32":
         return "fwd_f32"
+    if w.d == 128:  # every fp16 / bf16 launch at d = 128
+        return "fwd_pipe"
     # rows per workgroup and workgroups per CU of the one-wave-per-SIMD kernel
     if w.d in (64, 128) and w.causal and (w.N + 511) // 512 * w.B * w.H >= 2 * 256:
         return "fwd_wide (long causal)"

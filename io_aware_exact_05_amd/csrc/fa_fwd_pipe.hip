@@ -256,14 +256,18 @@ void fwd_pipe(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int s = 0; s < kNS; ++s) asm volatile("" ::"v"(qop[qb][s]));  // Q (and every copy) has landed
+    for (int s = 0; s < kNS; ++s) asm volatile("" ::"v"(qop[qb][s]));  // Q has landed
   if (p.scale_log2 < 0.f) {  // a negative scale moves into Q's sign (exact)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int s = 0; s < kNS; ++s) qop[qb][s] ^= (int)0x80008000u;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Copies land in issue order: once only the last ST - 2 groups (K(t), V(t-1)
+  // for t = 2 .. ST-1) may be in flight, K0, K1 and V0 are in LDS, which is
+  // all that S(0) and phase A of iteration 0 read; the first barrier waits
+  // for K2 and V1.
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPT * (ST - 2)) : "memory");
   __syncthreads();
 
   if (jlast >= 0) {
