@@ -51,7 +51,10 @@ void decode_partial(DecodeParams p) {
   constexpr int RB = 2 * D, TB = BC * RB, CPR = D / 8, CPT = BC * CPR / 64;
   constexpr int NS = D / 16, ND = D / 32;
   constexpr int WB = ST * 2 * TB;                      // ring bytes per wave
-  static_assert(32 * D * 4 + 256 <= WB, "the merge area must fit in a wave's ring");
+  // Merge rows are D + 4 floats apart, so the rows of a half wave start 4
+  // banks apart: 16-byte accesses of 16 rows cover the 64 banks once.
+  constexpr int MS = D + 4;
+  static_assert(32 * MS * 4 + 256 <= WB, "the merge area must fit in a wave's ring");
   __shared__ __attribute__((aligned(1024))) char smem[NW * WB];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -208,14 +211,14 @@ void decode_partial(DecodeParams p) {
   // ---- merge the waves' partial results in LDS (each wave's ring area) ----
   const float lt = pair_sum(l);
   __syncthreads();  // every wave is done with its ring
-  float* mo = (float*)ring;                   // [32 rows][D] unnormalised O of this wave
-  float* ml = (float*)(ring + 32 * D * 4);    // [32] m, then [32] l
+  float* mo = (float*)ring;                   // [32 rows][MS] unnormalised O of this wave
+  float* ml = (float*)(ring + 32 * MS * 4);   // [32] m, then [32] l
 #pragma unroll
   for (int bb = 0; bb < ND; ++bb)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       float4 v4 = {oacc[bb][4 * a], oacc[bb][4 * a + 1], oacc[bb][4 * a + 2], oacc[bb][4 * a + 3]};
-      *(float4*)(mo + ql * D + 32 * bb + 8 * a + 4 * g) = v4;
+      *(float4*)(mo + ql * MS + 32 * bb + 8 * a + 4 * g) = v4;
     }
   if (g == 0) {
     ml[ql] = m;
@@ -228,42 +231,51 @@ void decode_partial(DecodeParams p) {
   float mw[NW], M = kMInit;
 #pragma unroll
   for (int u = 0; u < NW; ++u) {
-    mw[u] = ((const float*)(smem + u * WB + 32 * D * 4))[row];
+    mw[u] = ((const float*)(smem + u * WB + 32 * MS * 4))[row];
     M = fmaxf(M, mw[u]);
   }
   float L = 0.f, wt[NW];
 #pragma unroll
   for (int u = 0; u < NW; ++u) {
     wt[u] = __builtin_amdgcn_exp2f(mw[u] - M);
-    L += wt[u] * ((const float*)(smem + u * WB + 32 * D * 4))[32 + row];
+    L += wt[u] * ((const float*)(smem + u * WB + 32 * MS * 4))[32 + row];
   }
   const int rrho = rb * 32 + row;
   if (rrho >= p.R) return;
   const size_t orow = row_base + rrho;
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const float lse = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f : kNegInf;
+  static_assert(CPL % 4 == 0, "columns per thread in 16-byte groups");
+  // weighted sum over the waves of 4 columns (16-byte LDS reads)
+  auto combine4 = [&](int cc) __attribute__((always_inline)) {
+    float4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+      const float4 v = *(const float4*)((const float*)(smem + u * WB) + row * MS + col0 + cc);
+      x.x += wt[u] * v.x;
+      x.y += wt[u] * v.y;
+      x.z += wt[u] * v.z;
+      x.w += wt[u] * v.w;
+    }
+    return x;
+  };
   if (p.nsplit == 1) {
     T* out = (T*)p.o + orow * D + col0;
 #pragma unroll
-    for (int cc = 0; cc < CPL; cc += 2) {
-      float x0 = 0.f, x1 = 0.f;
-#pragma unroll
-      for (int u = 0; u < NW; ++u) {
-        const float* src = (const float*)(smem + u * WB) + row * D + col0 + cc;
-        x0 += wt[u] * src[0];
-        x1 += wt[u] * src[1];
-      }
-      *(uint32_t*)(out + cc) = Half<T>::pack2(x0 * inv, x1 * inv);
+    for (int cc = 0; cc < CPL; cc += 4) {
+      const float4 x = combine4(cc);
+      uint2 pk2;
+      pk2.x = Half<T>::pack2(x.x * inv, x.y * inv);
+      pk2.y = Half<T>::pack2(x.z * inv, x.w * inv);
+      *(uint2*)(out + cc) = pk2;
     }
     if (col0 == 0) p.lse[orow] = lse;
   } else {
     float* out = p.ws_o + (orow * p.nsplit + split) * D + col0;
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) {
-      float x = 0.f;
-#pragma unroll
-      for (int u = 0; u < NW; ++u) x += wt[u] * ((const float*)(smem + u * WB))[row * D + col0 + cc];
-      out[cc] = x * inv;
+    for (int cc = 0; cc < CPL; cc += 4) {
+      const float4 x = combine4(cc);
+      *(float4*)(out + cc) = float4{x.x * inv, x.y * inv, x.z * inv, x.w * inv};
     }
     if (col0 == 0) p.ws_lse[orow * p.nsplit + split] = lse;
   }
