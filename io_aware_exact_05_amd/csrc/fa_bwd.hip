@@ -271,22 +271,26 @@ void bwd_dq(BwdParams p) {
   const int nt = (kv_end + BC - 1) / BC;
   const int jlast = qrow0 >= N ? -1 : CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1;
 
-  int ld_off[CPT], ld_row[CPT];
+  // Tile copies through buffer resources bounded by the head: key rows past
+  // N read as zeros (their scores are masked, and zero K rows add nothing to
+  // dQ), and a copy's address is a constant per-lane offset plus the tile's.
+  uint32_t ld_voff[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int s = (u * NW + w) * 64 + lane, row = s / CPR, c = s % CPR;
-    ld_row[u] = row;
-    ld_off[u] = (c ^ chunk_swz<D>(row)) * 8;
+    ld_voff[u] = (uint32_t)(row * RB + (c ^ chunk_swz<D>(row)) * 16);
   }
+  const __amdgpu_buffer_rsrc_t kbuf = make_rsrc(kh, (uint32_t)N * RB);
+  const __amdgpu_buffer_rsrc_t vbuf = make_rsrc(vh, (uint32_t)N * RB);
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
   auto issue_tile = [&](int j, int stage) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + stage * 2 * TB;
+    const uint32_t t0 = (uint32_t)j * TB;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const size_t row = (size_t)min(j * BC + ld_row[u], N - 1);
       const uint32_t lo = dst + (u * NW + w) * 1024;
-      dma16(kh + row * D + ld_off[u], lo);
-      dma16(vh + row * D + ld_off[u], lo + TB);
+      buf_dma16(kbuf, t0 + ld_voff[u], lo);
+      buf_dma16(vbuf, t0 + ld_voff[u], lo + TB);
     }
   };
 
@@ -319,15 +323,23 @@ void bwd_dq(BwdParams p) {
         const f32x16 dp = mm_rows<T, D>(sv + kb * 32 * RB, G, dop);
         // register r holds key key0 + 16 (r/8) + r%8
         const int key0 = j * BC + kb * 32 + 8 * g;
-        // visible iff 16 (r/8) + r%8 <= rel; rel >= 31 when no key of the
-        // block is hidden from this lane (one select per score, no branch)
+        // visible iff 16 (r/8) + r%8 <= rel.  Only blocks that reach past N
+        // or (causal) past the wave's first row hide keys; the test is
+        // wave-uniform, so other blocks skip the selects.
         const int rel = (CAUSAL ? min(myq, N - 1) : N - 1) - key0;
+        const bool hides = j * BC + kb * 32 + 31 > (CAUSAL ? min(qrow0, N - 1) : N - 1);
+        if (hides) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-          pr = (16 * (r >> 3) + (r & 7) <= rel) ? pr : 0.f;
-          s[r] = pr * (dp[r] - dl);
+          for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+            s[r] = (16 * (r >> 3) + (r & 7) <= rel) ? pr : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dl);
         mm_tr<T, D>(sk + kb * 32 * RB, G, s, acc);
       }
     }
@@ -402,12 +414,13 @@ void bwd_dkdv(BwdParams p) {
   const int cnt = nqt - qs;
   const int ntile = grp * cnt;
 
-  int ld_off[CPT], ld_row[CPT];
+  // Q and dO tiles through buffer resources bounded by the query head:
+  // rows past N read as zeros (their base-2 lse is +inf, so P = 0 there).
+  uint32_t ld_voff[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int s = (u * NW + w) * 64 + lane, row = s / CPR, cc = s % CPR;
-    ld_row[u] = row;
-    ld_off[u] = (cc ^ chunk_swz<D>(row)) * 8;
+    ld_voff[u] = (uint32_t)(row * RB + (cc ^ chunk_swz<D>(row)) * 16);
   }
   // statistics chunk of this lane (lanes < SL): chunk w SL + lane of
   // [lse2 (BQ floats), D (BQ floats)]
@@ -419,15 +432,15 @@ void bwd_dkdv(BwdParams p) {
     const int hh = j / cnt, qt = qs + j % cnt;
     const int bhq = qh0 + hh;
     const size_t hq = (size_t)bhq * N * D;
-    const T* qsrc = (const T*)p.q + hq;
-    const T* dsrc = (const T*)p.dout + hq;
+    const __amdgpu_buffer_rsrc_t qbuf = make_rsrc((const T*)p.q + hq, (uint32_t)N * RB);
+    const __amdgpu_buffer_rsrc_t dbuf = make_rsrc((const T*)p.dout + hq, (uint32_t)N * RB);
     const uint32_t dst = smem_base + stage * STB;
+    const uint32_t t0 = (uint32_t)qt * TB;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const size_t row = (size_t)min(qt * BQ + ld_row[u], N - 1);
       const uint32_t lo = dst + (u * NW + w) * 1024;
-      dma16(qsrc + row * D + ld_off[u], lo);
-      dma16(dsrc + row * D + ld_off[u], lo + TB);
+      buf_dma16(qbuf, t0 + ld_voff[u], lo);
+      buf_dma16(dbuf, t0 + ld_voff[u], lo + TB);
     }
     if (lane < SL) dma16(s_src + (size_t)bhq * p.Npad + qt * BQ, dst + 2 * TB + w * SL * 16);
   };
@@ -477,7 +490,9 @@ void bwd_dkdv(BwdParams p) {
           dd[8 * hh + 0] = b0.x; dd[8 * hh + 1] = b0.y; dd[8 * hh + 2] = b0.z; dd[8 * hh + 3] = b0.w;
           dd[8 * hh + 4] = b1.x; dd[8 * hh + 5] = b1.y; dd[8 * hh + 6] = b1.z; dd[8 * hh + 7] = b1.w;
         }
-        // causal: visible iff 16 (r/8) + r%8 >= lo (one select per score)
+        // causal: visible iff 16 (r/8) + r%8 >= lo (one select per score: a
+        // branch around the selects costs this kernel's register allocation
+        // spills at d = 128)
         const int lo = mykey - (q0 + 32 * qb + 8 * g);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

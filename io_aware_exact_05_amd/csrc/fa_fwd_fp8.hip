@@ -18,13 +18,19 @@
 //             E8M0 block scale of the V^T operand, f is folded into P.  The
 //             block quantiser of this library emits powers of two (f = 1),
 //             for which the whole descale is applied without rounding.
-//   P         the rounded P that feeds the second product is
-//             P~ = e4m3(exp2(t - m + 8 - lazy + log2 f)).  The running max
-//             moves once a tile exceeds it by lazy = 2 (log2 units), so
-//             P = exp2(t - m) <= 4 and P~ <= 2^8 < 448 never saturates, while
-//             typical P~ stay well above e4m3's subnormal range (2^-6).  The
-//             running sum l counts the unrounded P (l += sum P~ 2^(lazy - 8)
-//             / f), and O = O~ 2^(lazy - 8) / l.
+//   P         each row's P of a tile is scaled by a power of two to its own
+//             tile maximum before rounding: with sigma = ceil(tile max - m)
+//             the rounded P is P~ = e4m3(exp2(t - m + 8 - sigma + log2 f)),
+//             whose row maximum lies in (2^7, 2^8], so it never saturates
+//             (448), and a tile far below the running max keeps e4m3's full
+//             precision instead of falling into its subnormal range; the
+//             MFMA's per-lane E8M0 scale of the P~ operand, 2^(sigma - 8),
+//             undoes the shift exactly.  The running max m moves once a tile
+//             exceeds it by lazy = 2 (log2 units): a larger headroom would
+//             save rescales of O but leave the dominant key's P off a power
+//             of two, and its rounding then dominates the error of rows that
+//             a few keys decide.  The running sum l counts the unrounded P,
+//             and O = O~ / l.
 //   P V       O^T += V8^T P~^T with V8 read transposed from LDS by
 //             ds_read_b64_tr_b8 (lane i of a 16-lane group receives byte
 //             i % 8 of the rows addressed by lanes 2e + i/8, e = 0..7).
@@ -66,9 +72,10 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// Same product with A scaled by 2^(sa - 127) (sa an E8M0 biased exponent).
-__device__ __forceinline__ f32x16 mfma8_sa(i32x8 a, i32x8 b, f32x16 c, int sa) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127);
+// Same product with A scaled by 2^(sa - 127) and each lane's B block by
+// 2^(sb - 127) (E8M0 biased exponents; sa wave-uniform, sb per lane).
+__device__ __forceinline__ f32x16 mfma8_sab(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
@@ -156,21 +163,26 @@ void fwd_fp8(Fp8Params p) {
   const int jlast = qrow0 >= N ? -1 : (CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1);
 
   // ---- copies (as in the 16-bit kernel, D-byte rows) ----
-  int ld_row[CPT], ld_off[CPT];
+  // Buffer resources bounded by the head: rows past N read as zeros (their
+  // keys are masked), and a copy's address is a constant per-lane offset
+  // plus the tile's wave-uniform one.
+  uint32_t ld_voff[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int s = (u * NW + w) * 64 + lane, row = s / CPR, ch16 = s % CPR;
-    ld_row[u] = row;
-    ld_off[u] = (ch16 ^ swz8<D>(row)) * 16;
+    ld_voff[u] = (uint32_t)(row * RB + (ch16 ^ swz8<D>(row)) * 16);
   }
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const __amdgpu_buffer_rsrc_t kbuf = make_rsrc(kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t vbuf = make_rsrc(vh, head_bytes);
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
   auto issue_tile = [&](int j) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + (j % ST) * SB + w * 1024;
+    const uint32_t t0 = (uint32_t)j * TB;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const size_t row = (size_t)min(j * BC + ld_row[u], N - 1);
-      dma16(kh + row * D + ld_off[u], dst + u * NW * 1024);
-      dma16(vh + row * D + ld_off[u], dst + u * NW * 1024 + TB);
+      buf_dma16(kbuf, t0 + ld_voff[u], dst + u * NW * 1024);
+      buf_dma16(vbuf, t0 + ld_voff[u], dst + u * NW * 1024 + TB);
     }
   };
 
@@ -213,8 +225,9 @@ void fwd_fp8(Fp8Params p) {
   };
 
   // ---- scale, mask, online softmax of tile j; P~ packed to e4m3 ----
-  // Rescales O when the running max moves; returns the tile's V scale (E8M0).
-  auto softmax = [&](int j, f32x16 (&S)[NKB], i32x8 (&P)[NKS]) __attribute__((always_inline)) -> int {
+  // Rescales O when the running max moves; returns the tile's V scale
+  // (E8M0) and sets this lane's P~ scale sb (E8M0).
+  auto softmax = [&](int j, f32x16 (&S)[NKB], i32x8 (&P)[NKS], int& sb) __attribute__((always_inline)) -> int {
     const int key0 = j * BC;
     const int blk = (j * BC) >> 7;  // the 128-row descale block of tile j
     const float ct = cq * kd[blk];
@@ -252,8 +265,16 @@ void fwd_fp8(Fp8Params p) {
     const float mant = __builtin_amdgcn_frexp_mantf(vdj);  // [1/2, 1)
     const float f = (mant == 0.5f) ? 1.0f : mant;
     ex -= (mant == 0.5f) ? 1 : 0;
-    const float beta = (8.0f - kLazy8) + __builtin_amdgcn_logf(f) - m;
-    const float lsc = __builtin_amdgcn_exp2f(kLazy8 - 8.0f) / f;
+    // this row's shift: its tile maximum in (2^7, 2^8] before rounding.
+    // sigma <= lazy after the update above; below -100 the tile's P are
+    // under 2^-100 of P's at the running max and any shift serves, as for
+    // rows with no visible key (P = 0).  The scale 127 + sigma - 8 then lies
+    // in [19, 129], a valid E8M0 exponent.
+    const float sig = (mt == kNegInf) ? 0.0f : fmaxf(__builtin_ceilf(mt - m), -100.0f);
+    const int isig = (int)sig;
+    sb = 127 + isig - 8;
+    const float beta = (8.0f - sig) + __builtin_amdgcn_logf(f) - m;
+    const float lsc = __builtin_amdgcn_ldexpf(__builtin_amdgcn_rcpf(f), isig - 8);
     float rs4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -281,8 +302,8 @@ void fwd_fp8(Fp8Params p) {
     return min(max(127 + ex, 0), 254);
   };
 
-  // ---- O^T += V8^T P~^T for the tile in stage st, V scale sa ----
-  auto pv = [&](int st, const i32x8 (&P)[NKS], int sa) __attribute__((always_inline)) {
+  // ---- O^T += V8^T P~^T for the tile in stage st, V scale sa, P~ scale sb ----
+  auto pv = [&](int st, const i32x8 (&P)[NKS], int sa, int sb) __attribute__((always_inline)) {
     const char* sv = smem + st * SB + TB;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -299,7 +320,7 @@ void fwd_fp8(Fp8Params p) {
           }
         const i32x8 va = {part[0][0], part[0][1], part[1][0], part[1][1],
                           part[2][0], part[2][1], part[3][0], part[3][1]};
-        oacc[b] = mfma8_sa(va, P[ks], oacc[b], sa);
+        oacc[b] = mfma8_sab(va, P[ks], oacc[b], sa, sb);
       }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -340,21 +361,21 @@ void fwd_fp8(Fp8Params p) {
   const bool upper = PP && w >= NW / 2;
   f32x16 S[NKB];
   i32x8 P[NKS];
-  int sa = 127;
+  int sa = 127, sb = 127;
   auto step = [&](int j, auto LAG) __attribute__((always_inline)) {
     const int st = j % ST;
     if (j + PD < nt) issue_tile(j + PD);
     if constexpr (!decltype(LAG)::value) {
       if (j <= jlast) {
         qk(st, S);
-        sa = softmax(j, S, P);
-        pv(st, P, sa);
+        sa = softmax(j, S, P, sb);
+        pv(st, P, sa, sb);
       }
     } else {
-      if (j >= 1 && j - 1 <= jlast) pv((j + ST - 1) % ST, P, sa);
+      if (j >= 1 && j - 1 <= jlast) pv((j + ST - 1) % ST, P, sa, sb);
       if (j <= jlast) {
         qk(st, S);
-        sa = softmax(j, S, P);
+        sa = softmax(j, S, P, sb);
       }
     }
     if (j + PD < nt) {  // steady state: tiles j + 2 .. j + PD may stay in flight
@@ -373,7 +394,7 @@ void fwd_fp8(Fp8Params p) {
     for (int j = 0; j < nsteps; ++j) step(j, std::false_type());
   }
 
-  // ---- epilogue: O = O~ 2^(lazy - 8) / l, LSE = ln2 (m + log2 l) ----
+  // ---- epilogue: O = O~ / l, LSE = ln2 (m + log2 l) ----
   // A lane holds one query's O row in 8-byte pieces; each wave stages its 32
   // bf16 rows in LDS (the ring is idle after the last barrier) and writes
   // whole 2D-byte rows, 16-byte chunks XOR-swizzled by row.
@@ -381,7 +402,7 @@ void fwd_fp8(Fp8Params p) {
   static_assert(NW * 32 * ORB <= ST * SB, "staging fits in the ring");
   char* stg = smem + w * (32 * ORB);
   const float lt = pair_sum(l);
-  const float inv = __builtin_amdgcn_exp2f(kLazy8 - 8.0f) / lt;
+  const float inv = 1.0f / lt;
 #pragma unroll
   for (int b = 0; b < ND; ++b)
 #pragma unroll
