@@ -137,11 +137,8 @@ template <> struct Half<__bf16> {
     f32x2 v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
-  // acc + the two values of a packed pair (exact: bf16 values are fp32 values)
-  static __device__ __forceinline__ float sum2(uint32_t x, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
-  }
+  // x rounded to bf16 (nearest even, as pack2), returned as fp32
+  static __device__ __forceinline__ float round1(float x) { return (float)(__bf16)x; }
 };
 template <> struct Half<_Float16> {
   static __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
@@ -152,10 +149,7 @@ template <> struct Half<_Float16> {
     f32x2 v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
-  static __device__ __forceinline__ float sum2(uint32_t x, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
-  }
+  static __device__ __forceinline__ float round1(float x) { return (float)(_Float16)x; }
 };
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row.  Rows of 256 B

@@ -190,15 +190,17 @@ void fwd_pipe(FwdParams p) {
     for (int b = 0; b < kND; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][b][r] = 0.f;
-  // l: fp32 sum of P (for the LSE); lr: sum of the rounded P that enters
-  // P V (O is divided by it, so a row dominated by one key gets that key's
-  // value row back without the rounding of its weight).
-  float m[QB], l[QB], lr[QB], alpha[QB];
+  // l: fp32 sum of P (for the LSE).  E: sum over tiles of the rounding
+  // error of each tile's largest P, in the units of l; O is divided by
+  // l + E, so the weight of a row's dominant key (its tile's largest P) is
+  // counted in the divisor exactly as it entered P V and such a row gets
+  // that key's value row back without the rounding of its weight.
+  float m[QB], l[QB], E[QB], alpha[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = kMInit;
     l[qb] = 0.f;
-    lr[qb] = 0.f;
+    E[qb] = 0.f;
     alpha[qb] = 1.f;
   }
   bool rescale_pending = false;
@@ -230,12 +232,17 @@ void fwd_pipe(FwdParams p) {
   };
 
   // Lazy running-max update of query block qb from its tile maximum mx
-  // (lane-local; combined with the partner lane here).
+  // (lane-local; combined with the partner lane here), and the rounding
+  // error of the tile's largest P (the same exponent argument as its
+  // exponential: one FMA of the raw score).
   auto max_update = [&](int qb, float mx) __attribute__((always_inline)) {
-    const float mt = pair_max(mx) * c;
+    const float mxp = pair_max(mx);
+    const float mt = mxp * c;
     const float mnew = (mt > m[qb] + kLazy) ? mt : m[qb];
     alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mnew);
     m[qb] = mnew;
+    const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf(mxp, c, -mnew));
+    E[qb] = __builtin_fmaf(E[qb], alpha[qb], Half<T>::round1(pm) - pm);
   };
 
   // ================= prologue =================
@@ -373,17 +380,6 @@ void fwd_pipe(FwdParams p) {
         const int kh = r >> 2, b = r & 3;  // kh: 16-key group of the tile
         oacc[qb][b] = Half<T>::mfma(vjoin(vop[r % VR]), pk[qb][kh >> 1][kh & 1], oacc[qb][b]);
       }
-      if (i < 8) {  // rounded row sums of P(j): 2 packed registers per slot
-        constexpr int PPQ = 8 * NKB;  // packed registers per query block
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int n = 2 * i + h, q = n / PPQ, nn = n % PPQ;
-          float acc = nn == 0 ? lr[q] * alpha[q] : lr[q];  // alpha of tile j until slot 8
-          acc = Half<T>::sum2((uint32_t)pk[q][nn / 8][(nn % 8) / 4][nn % 4], acc);
-          pin(acc);
-          lr[q] = acc;
-        }
-      }
       if constexpr (sm) {
         if (i < 8) {  // row maxima: 4 scores per slot
           const int f = 4 * i, q = f / SPQ;
@@ -493,7 +489,7 @@ void fwd_pipe(FwdParams p) {
   }
   for (j = jlast + 1; j < nt; ++j) barrier_step(j);
 
-  // ================= epilogue: O = O^T / lr, LSE = ln2 (m + log2 l) =================
+  // ================= epilogue: O = O^T / (l + E), LSE = ln2 (m + log2 l) =================
   // Every copy (including the zero-filled ones past the end) has landed and
   // every wave is done with the rings before they become the staging area.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -505,7 +501,7 @@ void fwd_pipe(FwdParams p) {
   for (int qb = 0; qb < QB; ++qb) {
     const int myq = qrow0 + 32 * qb + ql;
     const float lt = pair_sum(l[qb]);
-    const float inv = 1.0f / pair_sum(lr[qb]);
+    const float inv = 1.0f / (lt + E[qb]);  // E is the same on both lanes of a row
 #pragma unroll
     for (int b = 0; b < kND; ++b)
 #pragma unroll
