@@ -25,6 +25,15 @@
 // program order.  Score layout (S^T = K Q^T, one query per lane), key
 // permutation, transposed V reads, chunk swizzle and lazy running max are
 // those of fwd_wide.
+//
+// Work items.  When the grid has at least as many pairs of query tiles as
+// there are CUs, a workgroup takes query tiles i and nq - 1 - i of one head
+// (the parallelism over query tiles of "FlashAttention-2 (BN)", section 2,
+// with the causal load of every workgroup equal: nq + 1 tiles' worth of key
+// tiles).  The second tile's first ST K tiles and ST - 1 V tiles are copied
+// by the first tile's last barriers, so its start costs only its Q load;
+// each wave writes its output rows through its own LDS staging area, apart
+// from the rings.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -72,7 +81,7 @@ __device__ __forceinline__ void pin(V& x) {
   asm volatile("" : "+v"(x));
 }
 
-template <typename T, bool CAUSAL, typename Cfg>
+template <typename T, bool CAUSAL, bool PAIR, typename Cfg>
 __global__ __launch_bounds__(64 * Cfg::NW) __attribute__((amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fwd_pipe(FwdParams p) {
   constexpr int QB = Cfg::QB, BC = Cfg::BC, NW = Cfg::NW, ST = Cfg::ST, KR = Cfg::KR, VR = Cfg::VR;
@@ -85,19 +94,34 @@ void fwd_pipe(FwdParams p) {
   constexpr int NSC = QB * NKB * 16;            // scores per lane per tile
   constexpr int SPQ = NKB * 16;                 // scores per lane and query block
   constexpr int VBASE = ST * TB;                // V ring after the K ring
+  constexpr int SGB = 32 * kRB / 2;             // staging bytes per wave: 32 rows, half of d
   static_assert(NK * QB == 16 && NV * QB == 16, "16 MFMA slots per phase");
   static_assert(NSC == 32, "32 scores per lane and tile");
   static_assert(CPT * 64 * NW == BC * kCPR, "tile must split evenly over the waves");
   static_assert(ST % 2 == 0 && ST >= 4 && ST <= 8, "the loop is unrolled over the ring");
   static_assert(2 * CPT * (ST - 3) <= 15, "copies in flight at a barrier");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * ST * TB];
+  static_assert(!PAIR || (BR / BC) % ST == 0, "a causal first item spans a whole number of ring turns");
+  // K ring, V ring, then one output staging area per wave, apart from the
+  // rings so that a wave can write out one query tile while the copies of
+  // the next tile's first K/V tiles are still landing.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * ST * TB + NW * SGB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, g = lane >> 5;
   const int N = p.N;
-  int bh, qt;
-  decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt, 0);
+  // Work items: one query tile, or (PAIR) query tiles i and nq - 1 - i of one
+  // head, i first; with causal masking every pair then holds nq + 1 tiles'
+  // worth of key tiles, so all workgroups carry the same load.
+  int bh, qt, qt2 = -1;
+  if constexpr (PAIR) {
+    int pi;
+    decode_block(blockIdx.x, p.BH, (p.nq + 1) / 2, false, bh, pi, 0);
+    qt = pi;
+    if (p.nq - 1 - pi != pi) qt2 = p.nq - 1 - pi;
+  } else {
+    decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt, 0);
+  }
 
   const size_t head = (size_t)bh * N * kD;
   const T* __restrict__ qh = (const T*)p.q + head;
@@ -108,63 +132,86 @@ void fwd_pipe(FwdParams p) {
   // With two waves per SIMD (w and w + NW/2) and causal masking, each SIMD
   // gets one early and one late row block so the diagonal work spreads evenly.
   const int rblk = (CAUSAL && NW == 8 && w >= NW / 2) ? (NW + NW / 2 - 1 - w) : w;
-  const int qrow0 = qt * BR + rblk * WR;
   const float c = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
 
-  const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
-  const int nt = (kv_end + BC - 1) / BC;
-  const int jlast = qrow0 >= N ? -1 : (CAUSAL ? min(nt - 1, (qrow0 + WR - 1) / BC) : nt - 1);
+  // Per-item geometry: first query row of this wave, key tiles of the
+  // workgroup (nt) and of this wave (jlast: its last key tile, -1: none).
+  int qrow0, nt, jlast;
+  auto set_item = [&](int t) __attribute__((always_inline)) {
+    qrow0 = t * BR + rblk * WR;
+    const int kv_end = CAUSAL ? min(N, (t + 1) * BR) : N;
+    nt = (kv_end + BC - 1) / BC;
+    jlast = qrow0 >= N ? -1 : (CAUSAL ? min(nt - 1, (qrow0 + WR - 1) / BC) : nt - 1);
+  };
+  set_item(qt);
+  bool has_next = qt2 >= 0;  // wave-uniform
 
   // ---- tile copies (wave w, instruction u fills LDS slots (u NW + w) 64 + lane) ----
-  uint32_t ld_voff[CPT];
+  // Per-lane byte offsets of the copies (ld_voff) and LDS base addresses of
+  // the K and V^T operand reads (kaddr, vaddr), kept in registers: the ring
+  // stage and tile offsets then fit the instructions' 16-bit immediate
+  // offsets.  Computed afresh for each work item from a lane index the
+  // compiler cannot see through, so none of them stays live across items.
+  uint32_t ld_voff[CPT], kaddr[kNS], vaddr[2][4];
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+  auto set_addrs = [&]() __attribute__((always_inline)) {
+    int ln = lane;
+    pin(ln);
+    const int lq = ln & 31, lg = ln >> 5;
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    const int s = (u * NW + w) * 64 + lane, row = s / kCPR, ch = s % kCPR;
-    ld_voff[u] = row * kRB + (ch ^ chunk_swz<kD>(row)) * 16;
-  }
+    for (int u = 0; u < CPT; ++u) {
+      const int s = (u * NW + w) * 64 + ln, row = s / kCPR, ch = s % kCPR;
+      ld_voff[u] = row * kRB + (ch ^ chunk_swz<kD>(row)) * 16;
+    }
+    const int krow = swap_bits23(lq);
+    const int kbase = krow * kRB + ((lg ^ chunk_swz<kD>(krow)) << 4);
+    const int trow = (ln & 15) >> 2;
+    const int vrow = 8 * lg + trow;
+    const int vaddr0 = vrow * kRB + 8 * (ln & 1) +
+                       (((2 * ((ln >> 4) & 1) + ((ln & 3) >> 1)) ^ chunk_swz<kD>(vrow)) << 4);
+    const int vaddr1 = vaddr0 ^ (4 * kRB + 16);
+#pragma unroll
+    for (int s2 = 0; s2 < kNS; ++s2) {
+      kaddr[s2] = smem_base + (uint32_t)(kbase ^ (s2 << 5));
+      pin(kaddr[s2]);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      vaddr[0][b] = smem_base + VBASE + (uint32_t)(vaddr0 ^ (b << 6));
+      vaddr[1][b] = smem_base + VBASE + (uint32_t)(vaddr1 ^ (b << 6));
+      pin(vaddr[0][b]);
+      pin(vaddr[1][b]);
+    }
+  };
+  set_addrs();
   const uint32_t head_bytes = (uint32_t)N * kRB;
   const __amdgpu_buffer_rsrc_t kbuf = make_rsrc(kh, head_bytes);
   const __amdgpu_buffer_rsrc_t vbuf = make_rsrc(vh, head_bytes);
-  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
-  // Tiles past the end of the head read as zeros (hardware range check), so
-  // every barrier issues the same number of copies and the wait counts stay
-  // constant.
+  const __amdgpu_buffer_rsrc_t obuf = make_rsrc((const T*)p.o + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t lbuf = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4u);
+  // Tile t of the current item sits in ring stage t % ST.  Past the item's
+  // last tile the copies continue with the next item's first tiles (same
+  // head; the first item's tile count is a multiple of ST, so they land in
+  // the stages the next item expects), or, after the last item, read as
+  // zeros (hardware range check): every barrier issues the same number of
+  // copies and the wait counts stay constant.
+  auto tile_off = [&](int t) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)((t >= nt && has_next) ? t - nt : t) * TB;
+  };
   auto issue_k = [&](int t) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + (uint32_t)(t % ST) * TB + w * 1024;
-    const uint32_t t0 = (uint32_t)t * TB;
+    const uint32_t t0 = tile_off(t);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) buf_dma16(kbuf, t0 + ld_voff[u], dst + u * NW * 1024);
   };
   auto issue_v = [&](int t) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + VBASE + (uint32_t)(t % ST) * TB + w * 1024;
-    const uint32_t t0 = (uint32_t)t * TB;
+    const uint32_t t0 = tile_off(t);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) buf_dma16(vbuf, t0 + ld_voff[u], dst + u * NW * 1024);
   };
 
-  // ---- LDS read geometry (as in fwd_wide) ----
-  const int krow = swap_bits23(ql);
-  const int kbase = krow * kRB + ((g ^ chunk_swz<kD>(krow)) << 4);
-  const int trow = (lane & 15) >> 2;
-  const int vrow = 8 * g + trow;
-  const int vaddr0 = vrow * kRB + 8 * (lane & 1) +
-                     (((2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ chunk_swz<kD>(vrow)) << 4);
-  const int vaddr1 = vaddr0 ^ (4 * kRB + 16);
-  // Per-lane LDS base addresses, kept in registers: the ring stage and tile
-  // offsets then fit the instructions' 16-bit immediate offsets.
-  uint32_t kaddr[kNS], vaddr[2][4];
-#pragma unroll
-  for (int s2 = 0; s2 < kNS; ++s2) {
-    kaddr[s2] = smem_base + (uint32_t)(kbase ^ (s2 << 5));
-    pin(kaddr[s2]);
-  }
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    vaddr[0][b] = smem_base + VBASE + (uint32_t)(vaddr0 ^ (b << 6));
-    vaddr[1][b] = smem_base + VBASE + (uint32_t)(vaddr1 ^ (b << 6));
-    pin(vaddr[0][b]);
-    pin(vaddr[1][b]);
-  }
+  // LDS read geometry (as in fwd_wide): see set_addrs.
 
   // K operand r of a tile (r = s NKB + kb: k-step s, key block kb).
   auto kread = [&](int stage, int r) __attribute__((always_inline)) -> i32x4 {
@@ -184,26 +231,37 @@ void fwd_pipe(FwdParams p) {
   };
   i32x4 qop[QB][kNS];
   f32x16 oacc[QB][kND];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int b = 0; b < kND; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qb][b][r] = 0.f;
   // l: fp32 sum of P (for the LSE).  E: sum over tiles of the rounding
   // error of each tile's largest P, in the units of l; O is divided by
   // l + E, so the weight of a row's dominant key (its tile's largest P) is
   // counted in the divisor exactly as it entered P V and such a row gets
   // that key's value row back without the rounding of its weight.
   float m[QB], l[QB], E[QB], alpha[QB];
+  bool rescale_pending;
+  auto reset_rows = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = kMInit;
-    l[qb] = 0.f;
-    E[qb] = 0.f;
-    alpha[qb] = 1.f;
-  }
-  bool rescale_pending = false;
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int b = 0; b < kND; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[qb][b][r] = 0.f;
+      m[qb] = kMInit;
+      l[qb] = 0.f;
+      E[qb] = 0.f;
+      alpha[qb] = 1.f;
+    }
+    rescale_pending = false;
+  };
+  // Q rows of the wave's query blocks starting at row q0 (rows past N
+  // repeat row N - 1; their results are never stored).
+  auto load_q = [&](int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const T* qr = qh + (size_t)min(q0 + 32 * qb + ql, N - 1) * kD + 8 * g;
+#pragma unroll
+      for (int s = 0; s < kNS; ++s) qop[qb][s] = *(const i32x4*)(qr + 16 * s);
+    }
+  };
 
   typedef f32x16 STile[QB][NKB];
   STile sa, sb;             // score tiles of alternate iterations
@@ -246,37 +304,58 @@ void fwd_pipe(FwdParams p) {
   };
 
   // ================= prologue =================
-  // Copies: K0, then Q (registers), then K(t), V(t-1) for t = 1 .. ST-1 (the
-  // groups the barriers before iteration 0 would have issued).
-  issue_k(0);
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const T* qr = qh + (size_t)min(qrow0 + 32 * qb + ql, N - 1) * kD + 8 * g;
-#pragma unroll
-    for (int s = 0; s < kNS; ++s) qop[qb][s] = *(const i32x4*)(qr + 16 * s);
-  }
-#pragma unroll
-  for (int t = 1; t < ST; ++t) {
-    issue_k(t);
-    issue_v(t - 1);
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int s = 0; s < kNS; ++s) asm volatile("" ::"v"(qop[qb][s]));  // Q has landed
-  if (p.scale_log2 < 0.f) {  // a negative scale moves into Q's sign (exact)
+  // K0, K1, V0 (what S(0) and phase A of iteration 0 read) and Q are waited
+  // for before the copies of K(t), V(t-1), t = 2 .. ST-1 (the groups the
+  // barriers before iteration 0 would have issued) start: the compiler's
+  // wait for Q counts only the loads it knows of, so later copies would be
+  // waited for as well.  The first barrier waits for K2 and V1.
+  auto q_landed = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int s = 0; s < kNS; ++s) qop[qb][s] ^= (int)0x80008000u;
-  }
-  // Copies land in issue order: once only the last ST - 2 groups (K(t), V(t-1)
-  // for t = 2 .. ST-1) may be in flight, K0, K1 and V0 are in LDS, which is
-  // all that S(0) and phase A of iteration 0 read; the first barrier waits
-  // for K2 and V1.
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPT * (ST - 2)) : "memory");
+      for (int s = 0; s < kNS; ++s) asm volatile("" ::"v"(qop[qb][s]));  // the compiler waits here
+    if (p.scale_log2 < 0.f) {  // a negative scale moves into Q's sign (exact)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int s = 0; s < kNS; ++s) qop[qb][s] ^= (int)0x80008000u;
+    }
+  };
+  issue_k(0);
+  issue_k(1);
+  issue_v(0);
+  load_q(qrow0);
+  q_landed();
   __syncthreads();
+#pragma unroll
+  for (int t = 2; t < ST; ++t) {
+    issue_k(t);
+    issue_v(t - 1);
+  }
 
+  // ================= work items =================
+  auto run_item = [&]() __attribute__((always_inline)) {
+  if constexpr (PAIR) set_addrs();
+  // The previous item's score tiles and operands are dead; without this the
+  // compiler keeps them live into this item (it cannot tell that every read
+  // below follows a write of this item).
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      asm volatile("" : "=v"(sa[qb][kb]));
+      asm volatile("" : "=v"(sb[qb][kb]));
+      asm volatile("" : "=v"(pk[qb][kb][0]));
+      asm volatile("" : "=v"(pk[qb][kb][1]));
+    }
+#pragma unroll
+  for (int i = 0; i < KR; ++i) asm volatile("" : "=v"(kop[i]));
+#pragma unroll
+  for (int i = 0; i < VR; ++i) {
+    asm volatile("" : "=v"(vop[i][0]));
+    asm volatile("" : "=v"(vop[i][1]));
+  }
+  reset_rows();
   if (jlast >= 0) {
     // S(0), its maximum and exponent arguments; first K(1) operands.
     const f32x16 zero = {};
@@ -489,51 +568,90 @@ void fwd_pipe(FwdParams p) {
   }
   for (j = jlast + 1; j < nt; ++j) barrier_step(j);
 
+  // After the last item only the zero-filled copies of the last barriers
+  // are in flight: they land before the workgroup's LDS is released.
+  if (!has_next) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
   // ================= epilogue: O = O^T / (l + E), LSE = ln2 (m + log2 l) =================
-  // Every copy (including the zero-filled ones past the end) has landed and
-  // every wave is done with the rings before they become the staging area.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  static_assert(NW * 32 * kRB <= 2 * ST * TB, "staging fits in the rings");
-  char* stg = smem + w * (32 * kRB);
-  T* __restrict__ oh = (T*)p.o + head;
+  // Each wave stages its rows in its own LDS area, half of d at a time, and
+  // stores whole half rows.  Buffer stores with a resource over this head's
+  // rows: the range check drops rows past N.
+  char* stg = smem + 2 * ST * TB + w * SGB;
+  constexpr int HRB = kRB / 2, HC = kCPR / 2;  // bytes and 16-byte chunks per half row
+  int eln = lane;  // as in set_addrs: no offset below is shared between items
+  pin(eln);
+  const int eq = eln & 31, eg = eln >> 5;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int myq = qrow0 + 32 * qb + ql;
+    const int r0 = qrow0 + 32 * qb;
     const float lt = pair_sum(l[qb]);
     const float inv = 1.0f / (lt + E[qb]);  // E is the same on both lanes of a row
 #pragma unroll
-    for (int b = 0; b < kND; ++b)
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        uint2 stv;
-        stv.x = Half<T>::pack2(oacc[qb][b][4 * a] * inv, oacc[qb][b][4 * a + 1] * inv);
-        stv.y = Half<T>::pack2(oacc[qb][b][4 * a + 2] * inv, oacc[qb][b][4 * a + 3] * inv);
-        *(uint2*)(stg + ql * kRB + (((4 * b + a) ^ (ql & (kCPR - 1))) << 4) + 8 * g) = stv;
+      for (int bb = 0; bb < kND / 2; ++bb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int b = h * (kND / 2) + bb;
+          uint2 stv;
+          stv.x = Half<T>::pack2(oacc[qb][b][4 * a] * inv, oacc[qb][b][4 * a + 1] * inv);
+          stv.y = Half<T>::pack2(oacc[qb][b][4 * a + 2] * inv, oacc[qb][b][4 * a + 3] * inv);
+          *(uint2*)(stg + eq * HRB + (((4 * bb + a) ^ (eq & (HC - 1))) << 4) + 8 * eg) = stv;
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 32 * HC / 64; ++it) {
+        const int idx = it * 64 + eln, row = idx / HC, ch = idx % HC;
+        const i32x4 val = *(const i32x4*)(stg + row * HRB + ((ch ^ (row & (HC - 1))) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(val, obuf, (uint32_t)(r0 + row) * kRB + h * HRB + ch * 16, 0, 0);
       }
-    if (g == 0 && myq < N)
-      p.lse[(size_t)bh * N + myq] = (m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int it = 0; it < 32 * kCPR / 64; ++it) {
-      const int idx = it * 64 + lane, row = idx / kCPR, ch = idx % kCPR;
-      const i32x4 val = *(const i32x4*)(stg + row * kRB + ((ch ^ (row & (kCPR - 1))) << 4));
-      const int grow = qrow0 + 32 * qb + row;
-      if (grow < N) *(i32x4*)(oh + (size_t)grow * kD + ch * 8) = val;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next half's writes
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next block's writes
+    const float lse = (m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994530942f;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, lse), lbuf, (uint32_t)(r0 + eq) * 4u, 0, 0);
+  }
+  };
+  run_item();
+  if constexpr (PAIR) {
+    if (has_next) {
+      set_item(qt2);
+      has_next = false;
+      load_q(qrow0);
+      q_landed();
+      run_item();
+    }
   }
 }
 
 #undef FA_SREF
+
+// Query tiles i and nq - 1 - i go to one workgroup when that does not add a
+// round of workgroups per CU (the pairs' rounds take two items' time) and,
+// without masking, when a tile's key tiles fill whole turns of the ring.
+template <typename Cfg>
+bool pipe_pairs(const FwdParams& p, int nq, bool causal) {
+  if (nq < 2) return false;
+  if (!causal && ((p.N + Cfg::BC - 1) / Cfg::BC) % Cfg::ST != 0) return false;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return false;
+  const long long items = (long long)nq * p.BH, pairs = (long long)((nq + 1) / 2) * p.BH;
+  return 2 * ((pairs + cus - 1) / cus) <= (items + cus - 1) / cus;
+}
 
 template <typename T, bool CAUSAL, typename Cfg>
 hipError_t launch_pipe(const FwdParams& p, hipStream_t stream) {
   constexpr int BR = 32 * Cfg::QB * Cfg::NW;
   FwdParams q = p;
   q.nq = (p.N + BR - 1) / BR;
-  const unsigned grid = (unsigned)(q.nq * p.BH);
-  hipLaunchKernelGGL((fwd_pipe<T, CAUSAL, Cfg>), dim3(grid), dim3(64 * Cfg::NW), 0, stream, q);
+  if (pipe_pairs<Cfg>(q, q.nq, CAUSAL)) {
+    const unsigned grid = (unsigned)(((q.nq + 1) / 2) * p.BH);
+    hipLaunchKernelGGL((fwd_pipe<T, CAUSAL, true, Cfg>), dim3(grid), dim3(64 * Cfg::NW), 0, stream, q);
+  } else {
+    const unsigned grid = (unsigned)(q.nq * p.BH);
+    hipLaunchKernelGGL((fwd_pipe<T, CAUSAL, false, Cfg>), dim3(grid), dim3(64 * Cfg::NW), 0, stream, q);
+  }
   return hipGetLastError();
 }
 

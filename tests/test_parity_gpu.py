@@ -94,6 +94,30 @@ def test_long_causal_configuration_every_element(dtype, d, BH, N):
     check(o, lse, o_ref, lse_ref, dtype, f"{dtype} BH={BH} N={N} causal")
 
 
+# At d = 128, launches with at least as many query-tile pairs as CUs (and,
+# without masking, key-tile counts that are multiples of the 4-stage ring)
+# give each workgroup query tiles i and nq - 1 - i of one head, the second
+# one's first K/V tiles copied during the first one's last iterations.
+# Ragged N, the middle tile of an odd count alone (N = 600), GQA heads.
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,H,Hkv,N,causal", [(2, 128, 128, 512, 0), (2, 128, 128, 512, 1),
+                                              (1, 128, 128, 1000, 0), (1, 128, 128, 1000, 1),
+                                              (1, 128, 128, 600, 1), (2, 128, 16, 512, 1)])
+def test_paired_query_tiles_every_element(dtype, B, H, Hkv, N, causal):
+    _say(f"case paired tiles dtype={dtype} B={B} H={H} Hkv={Hkv} N={N} causal={causal}")
+    d = 128
+    q, _, _ = inputs.random_inputs(B, H, N, d, dtype, seed=B * H + N + causal)
+    _, k, v = inputs.random_inputs(B, Hkv, N, d, dtype, seed=B * Hkv + 3 * N)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    fa = _fa()
+    o, lse = fa.attention(q.cuda(), k.cuda(), v.cuda(), bool(causal), scale)
+    torch.cuda.synchronize()
+    rep = H // Hkv
+    kr, vr = np.repeat(widen(k), rep, axis=1), np.repeat(widen(v), rep, axis=1)
+    o_ref, lse_ref = oracle.attention(widen(q), kr, vr, causal, scale)
+    check(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype, f"{dtype} paired B={B} H={H} N={N} causal={causal}")
+
+
 FULL = [w for w in inputs.WORKLOADS if w.dtype != "e4m3"]
 
 
@@ -174,10 +198,10 @@ def test_deterministic_bitwise():
                 assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_every_output_written_and_no_out_of_bounds_writes(dtype):
-    _say(f"case poison/canary {dtype}")
-    B, H, N, d = 1, 3, 333, 128
+@pytest.mark.parametrize("dtype,B,H,N", [("bf16", 1, 3, 333), ("f32", 1, 3, 333), ("bf16", 1, 128, 1000)])
+def test_every_output_written_and_no_out_of_bounds_writes(dtype, B, H, N):
+    _say(f"case poison/canary {dtype} B={B} H={H} N={N}")
+    d = 128
     q, k, v = inputs.random_inputs(B, H, N, d, dtype, seed=13)
     fa = _fa()
     n, guard = B * H * N * d, 4096
