@@ -142,9 +142,13 @@ void fwd_fp8(Fp8Params p) {
   const uint8_t* __restrict__ qh = p.q + head;
   const uint8_t* __restrict__ kh = p.k + head;
   const uint8_t* __restrict__ vh = p.v + head;
-  const float* qd = p.q_descale + (size_t)bh * p.nblk;
-  const float* kd = p.k_descale + (size_t)bh * p.nblk;
-  const float* vd = p.v_descale + (size_t)bh * p.nblk;
+  // Descales are read through the constant address space: wave-uniform
+  // scalar loads, counted apart from the tile copies (a vector load here
+  // would make each tile's softmax wait for every copy in flight).
+  typedef const __attribute__((address_space(4))) float cfloat;
+  const cfloat* qd = (const cfloat*)(p.q_descale + (size_t)bh * p.nblk);
+  const cfloat* kd = (const cfloat*)(p.k_descale + (size_t)bh * p.nblk);
+  const cfloat* vd = (const cfloat*)(p.v_descale + (size_t)bh * p.nblk);
 
   const int qrow0 = qt * BR + w * 32;
   const int myq = qrow0 + ql;
