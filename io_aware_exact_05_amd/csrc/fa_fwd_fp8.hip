@@ -26,11 +26,13 @@
 //             precision instead of falling into its subnormal range; the
 //             MFMA's per-lane E8M0 scale of the P~ operand, 2^(sigma - 8),
 //             undoes the shift exactly.  The running max m moves once a tile
-//             exceeds it by lazy = 2 (log2 units): a larger headroom would
-//             save rescales of O but leave the dominant key's P off a power
-//             of two, and its rounding then dominates the error of rows that
-//             a few keys decide.  The running sum l counts the unrounded P,
-//             and O = O~ / l.
+//             exceeds it by lazy = 8 (log2 units; with the rare outlier
+//             entries of the fp8 workload a headroom of 2 rescaled O at half
+//             of the tiles).  The running sum l counts the unrounded P (it
+//             gives the logsumexp); E sums the rounding error of each tile's
+//             largest P~, and O = O~ / (l + E): a row that one key decides,
+//             whose P~ is off a power of two under the lazy max, gets that
+//             key's value row back without the rounding of its weight.
 //   P V       O^T += V8^T P~^T with V8 read transposed from LDS by
 //             ds_read_b64_tr_b8 (lane i of a 16-lane group receives byte
 //             i % 8 of the rows addressed by lanes 2e + i/8, e = 0..7).
@@ -48,7 +50,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef i32x2 __attribute__((address_space(3))) lds_i32x2;
 
-constexpr float kLazy8 = 2.0f;  // log2 headroom of the running max on this path
+constexpr float kLazy8 = 8.0f;  // log2 headroom of the running max on this path
 
 // XOR swizzle of the 16-byte chunk inside an fp8 row of D bytes; the value
 // is below D / 16, so XOR with it permutes the row's chunks.
@@ -81,6 +83,11 @@ __device__ __forceinline__ f32x16 mfma8_sab(i32x8 a, i32x8 b, f32x16 c, int sa, 
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// x rounded to e4m3 (the conversion that packs P~), returned as fp32
+__device__ __forceinline__ float round_e4m3(float x) {
+  return __builtin_amdgcn_cvt_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false), 0);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
@@ -206,7 +213,11 @@ void fwd_fp8(Fp8Params p) {
   for (int b = 0; b < ND; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
-  float m = kMInit, l = 0.f;
+  // l: fp32 sum of the unrounded P (for the LSE); E: sum over tiles of the
+  // rounding error of each tile's largest P~, in l's units.  O is divided by
+  // l + E, so a row that one key decides gets that key's value row back
+  // without the rounding of its weight.
+  float m = kMInit, l = 0.f, E = 0.f;
 
   // ---- S^T = K8 Q8^T for tile j (stage st) ----
   auto qk = [&](int st, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
@@ -257,6 +268,7 @@ void fwd_fp8(Fp8Params p) {
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
       m = mnew;
       l *= alpha;
+      E *= alpha;
 #pragma unroll
       for (int b = 0; b < ND; ++b)
 #pragma unroll
@@ -289,6 +301,9 @@ void fwd_fp8(Fp8Params p) {
         rs4[r & 3] += pr;
       }
     l += ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3])) * lsc;
+    // the row's largest P~ of this tile (0 if all keys are hidden)
+    const float pm = (mt == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(mx, ct, beta));
+    E = __builtin_fmaf(round_e4m3(pm) - pm, lsc, E);
     // P~ operand of k-step ks: bytes 16 kbh + 8 h + e <- S[2 ks + kbh][8 h + e]
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -406,7 +421,7 @@ void fwd_fp8(Fp8Params p) {
   static_assert(NW * 32 * ORB <= ST * SB, "staging fits in the ring");
   char* stg = smem + w * (32 * ORB);
   const float lt = pair_sum(l);
-  const float inv = 1.0f / lt;
+  const float inv = 1.0f / (lt + E);  // E is the same on both lanes of a row
 #pragma unroll
   for (int b = 0; b < ND; ++b)
 #pragma unroll
