@@ -27,13 +27,14 @@
 // those of fwd_wide.
 //
 // Work items.  When the grid has at least as many pairs of query tiles as
-// there are CUs, a workgroup takes query tiles i and nq - 1 - i of one head
-// (the parallelism over query tiles of "FlashAttention-2 (BN)", section 2,
-// with the causal load of every workgroup equal: nq + 1 tiles' worth of key
-// tiles).  The second tile's first ST K tiles and ST - 1 V tiles are copied
-// by the first tile's last barriers, so its start costs only its Q load;
-// each wave writes its output rows through its own LDS staging area, apart
-// from the rings.
+// there are CUs, a workgroup takes two (the parallelism over query tiles of
+// "FlashAttention-2 (BN)", section 2): with causal masking tiles i and
+// nq - 1 - i of one head, so that every workgroup's load is nq + 1 tiles'
+// worth of key tiles; without it the same tile of two heads of one XCD.
+// The second tile's first ST K tiles and ST - 1 V tiles are copied by the
+// first tile's last barriers, so its start costs only its Q load; each wave
+// writes its output rows through its own LDS staging area, apart from the
+// rings.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -110,24 +111,33 @@ void fwd_pipe(FwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, g = lane >> 5;
   const int N = p.N;
-  // Work items: one query tile, or (PAIR) query tiles i and nq - 1 - i of one
-  // head, i first; with causal masking every pair then holds nq + 1 tiles'
-  // worth of key tiles, so all workgroups carry the same load.
-  int bh, qt, qt2 = -1;
+  // Work items: one query tile, or (PAIR) two.  With causal masking, query
+  // tiles i and nq - 1 - i of one head, i first: every pair holds nq + 1
+  // tiles' worth of key tiles, so all workgroups carry the same load.
+  // Without masking (head count a multiple of 16), the same query tile of
+  // two heads of one XCD: an XCD's workgroups first run every tile of half
+  // of its heads, then every tile of the other half, so each head's K and V
+  // still stream from HBM once, shared in L2 by its query tiles.
+  int bh, qt, bh2 = -1, qt2 = -1;
   if constexpr (PAIR) {
-    int pi;
-    decode_block(blockIdx.x, p.BH, (p.nq + 1) / 2, false, bh, pi, 0);
-    qt = pi;
-    if (p.nq - 1 - pi != pi) qt2 = p.nq - 1 - pi;
+    if constexpr (CAUSAL) {
+      int pi;
+      decode_block(blockIdx.x, p.BH, (p.nq + 1) / 2, false, bh, pi, 0);
+      qt = pi;
+      if (p.nq - 1 - pi != pi) {
+        bh2 = bh;
+        qt2 = p.nq - 1 - pi;
+      }
+    } else {
+      const int hx = p.BH >> 3, loc = blockIdx.x >> 3;
+      bh = (blockIdx.x & 7) * hx + loc / p.nq;
+      qt = loc % p.nq;
+      bh2 = bh + hx / 2;
+      qt2 = qt;
+    }
   } else {
     decode_block(blockIdx.x, p.BH, p.nq, CAUSAL, bh, qt, 0);
   }
-
-  const size_t head = (size_t)bh * N * kD;
-  const T* __restrict__ qh = (const T*)p.q + head;
-  const size_t kvhead = (size_t)kv_head(p, bh) * N * kD;
-  const T* __restrict__ kh = (const T*)p.k + kvhead;
-  const T* __restrict__ vh = (const T*)p.v + kvhead;
 
   // With two waves per SIMD (w and w + NW/2) and causal masking, each SIMD
   // gets one early and one late row block so the diagonal work spreads evenly.
@@ -184,31 +194,48 @@ void fwd_pipe(FwdParams p) {
     }
   };
   set_addrs();
+  // Buffer resources over one head's rows: K and V of the current item and
+  // of the next one, O and the logsumexp of the current item.
   const uint32_t head_bytes = (uint32_t)N * kRB;
-  const __amdgpu_buffer_rsrc_t kbuf = make_rsrc(kh, head_bytes);
-  const __amdgpu_buffer_rsrc_t vbuf = make_rsrc(vh, head_bytes);
-  const __amdgpu_buffer_rsrc_t obuf = make_rsrc((const T*)p.o + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t lbuf = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4u);
-  // Tile t of the current item sits in ring stage t % ST.  Past the item's
-  // last tile the copies continue with the next item's first tiles (same
-  // head; the first item's tile count is a multiple of ST, so they land in
-  // the stages the next item expects), or, after the last item, read as
-  // zeros (hardware range check): every barrier issues the same number of
-  // copies and the wait counts stay constant.
-  auto tile_off = [&](int t) __attribute__((always_inline)) -> uint32_t {
-    return (uint32_t)((t >= nt && has_next) ? t - nt : t) * TB;
+  const T* qh;
+  __amdgpu_buffer_rsrc_t kbuf, vbuf, obuf, lbuf, kbuf_n, vbuf_n;
+  auto kv_rsrc = [&](int h, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr) __attribute__((always_inline)) {
+    const size_t kvhead = (size_t)kv_head(p, h) * N * kD;
+    kr = make_rsrc((const T*)p.k + kvhead, head_bytes);
+    vr = make_rsrc((const T*)p.v + kvhead, head_bytes);
   };
+  auto set_head = [&](int h) __attribute__((always_inline)) {
+    const size_t head = (size_t)h * N * kD;
+    qh = (const T*)p.q + head;
+    obuf = make_rsrc((const T*)p.o + head, head_bytes);
+    lbuf = make_rsrc(p.lse + (size_t)h * N, (uint32_t)N * 4u);
+  };
+  set_head(bh);
+  kv_rsrc(bh, kbuf, vbuf);
+  if constexpr (PAIR) {
+    if (has_next) kv_rsrc(bh2, kbuf_n, vbuf_n);
+  }
+  // Tile t of the current item sits in ring stage t % ST.  Past the item's
+  // last tile the copies continue with the next item's first tiles (the
+  // first item's tile count is a multiple of ST, so they land in the stages
+  // the next item expects), or, after the last item, read as zeros
+  // (hardware range check): every barrier issues the same number of copies
+  // and the wait counts stay constant.
   auto issue_k = [&](int t) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + (uint32_t)(t % ST) * TB + w * 1024;
-    const uint32_t t0 = tile_off(t);
+    const bool nx = PAIR && t >= nt && has_next;
+    const uint32_t t0 = (uint32_t)(nx ? t - nt : t) * TB;
+    const __amdgpu_buffer_rsrc_t r = nx ? kbuf_n : kbuf;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) buf_dma16(kbuf, t0 + ld_voff[u], dst + u * NW * 1024);
+    for (int u = 0; u < CPT; ++u) buf_dma16(r, t0 + ld_voff[u], dst + u * NW * 1024);
   };
   auto issue_v = [&](int t) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + VBASE + (uint32_t)(t % ST) * TB + w * 1024;
-    const uint32_t t0 = tile_off(t);
+    const bool nx = PAIR && t >= nt && has_next;
+    const uint32_t t0 = (uint32_t)(nx ? t - nt : t) * TB;
+    const __amdgpu_buffer_rsrc_t r = nx ? vbuf_n : vbuf;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) buf_dma16(vbuf, t0 + ld_voff[u], dst + u * NW * 1024);
+    for (int u = 0; u < CPT; ++u) buf_dma16(r, t0 + ld_voff[u], dst + u * NW * 1024);
   };
 
   // LDS read geometry (as in fwd_wide): see set_addrs.
@@ -615,6 +642,9 @@ void fwd_pipe(FwdParams p) {
   if constexpr (PAIR) {
     if (has_next) {
       set_item(qt2);
+      set_head(bh2);
+      kbuf = kbuf_n;
+      vbuf = vbuf_n;
       has_next = false;
       load_q(qrow0);
       q_landed();
@@ -625,18 +655,19 @@ void fwd_pipe(FwdParams p) {
 
 #undef FA_SREF
 
-// Query tiles i and nq - 1 - i go to one workgroup when that does not add a
-// round of workgroups per CU (the pairs' rounds take two items' time) and,
-// without masking, when a tile's key tiles fill whole turns of the ring.
+// Two query tiles go to one workgroup when that does not add a round of
+// workgroups per CU (the pairs' rounds take two items' time); without
+// masking, when the head count is a multiple of 16 (two heads per pair,
+// same XCD) and a tile's key tiles fill whole turns of the ring.
 template <typename Cfg>
 bool pipe_pairs(const FwdParams& p, int nq, bool causal) {
-  if (nq < 2) return false;
-  if (!causal && ((p.N + Cfg::BC - 1) / Cfg::BC) % Cfg::ST != 0) return false;
+  if (causal ? nq < 2 : (p.BH % 16 != 0 || ((p.N + Cfg::BC - 1) / Cfg::BC) % Cfg::ST != 0)) return false;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return false;
-  const long long items = (long long)nq * p.BH, pairs = (long long)((nq + 1) / 2) * p.BH;
+  const long long items = (long long)nq * p.BH;
+  const long long pairs = causal ? (long long)((nq + 1) / 2) * p.BH : items / 2;
   return 2 * ((pairs + cus - 1) / cus) <= (items + cus - 1) / cus;
 }
 
@@ -646,7 +677,7 @@ hipError_t launch_pipe(const FwdParams& p, hipStream_t stream) {
   FwdParams q = p;
   q.nq = (p.N + BR - 1) / BR;
   if (pipe_pairs<Cfg>(q, q.nq, CAUSAL)) {
-    const unsigned grid = (unsigned)(((q.nq + 1) / 2) * p.BH);
+    const unsigned grid = CAUSAL ? (unsigned)(((q.nq + 1) / 2) * p.BH) : (unsigned)(q.nq * (p.BH / 2));
     hipLaunchKernelGGL((fwd_pipe<T, CAUSAL, true, Cfg>), dim3(grid), dim3(64 * Cfg::NW), 0, stream, q);
   } else {
     const unsigned grid = (unsigned)(q.nq * p.BH);

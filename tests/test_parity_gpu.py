@@ -94,15 +94,18 @@ def test_long_causal_configuration_every_element(dtype, d, BH, N):
     check(o, lse, o_ref, lse_ref, dtype, f"{dtype} BH={BH} N={N} causal")
 
 
-# At d = 128, launches with at least as many query-tile pairs as CUs (and,
-# without masking, key-tile counts that are multiples of the 4-stage ring)
-# give each workgroup query tiles i and nq - 1 - i of one head, the second
-# one's first K/V tiles copied during the first one's last iterations.
-# Ragged N, the middle tile of an odd count alone (N = 600), GQA heads.
+# At d = 128, launches with at least as many pairs of query tiles as CUs
+# give each workgroup two tiles, the second one's first K/V tiles copied
+# during the first one's last iterations: with causal masking tiles i and
+# nq - 1 - i of one head, without it (head counts that are multiples of 16,
+# key-tile counts that are multiples of the 4-stage ring) the same tile of
+# two heads.  Ragged N, the middle tile of an odd count alone (N = 600),
+# GQA heads.
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("B,H,Hkv,N,causal", [(2, 128, 128, 512, 0), (2, 128, 128, 512, 1),
                                               (1, 128, 128, 1000, 0), (1, 128, 128, 1000, 1),
-                                              (1, 128, 128, 600, 1), (2, 128, 16, 512, 1)])
+                                              (1, 128, 128, 600, 1), (2, 128, 16, 512, 1),
+                                              (2, 128, 16, 512, 0)])
 def test_paired_query_tiles_every_element(dtype, B, H, Hkv, N, causal):
     _say(f"case paired tiles dtype={dtype} B={B} H={H} Hkv={Hkv} N={N} causal={causal}")
     d = 128
