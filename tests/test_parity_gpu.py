@@ -121,6 +121,18 @@ def test_paired_query_tiles_every_element(dtype, B, H, Hkv, N, causal):
     check(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype, f"{dtype} paired B={B} H={H} N={N} causal={causal}")
 
 
+# A negative scale moves into Q's sign bits, for the second query tile of a
+# pair as for the first.
+@pytest.mark.parametrize("causal", [0, 1])
+def test_paired_query_tiles_negative_scale(causal):
+    _say(f"case paired tiles negative scale causal={causal}")
+    B, H, N, d = 2, 128, 512, 128
+    q, k, v = inputs.random_inputs(B, H, N, d, "bf16", seed=77 + causal)
+    o, lse = run_gpu(q, k, v, causal, -0.3)
+    o_ref, lse_ref = oracle.attention(widen(q), widen(k), widen(v), causal, -0.3)
+    check(o, lse, o_ref, lse_ref, "bf16", f"paired negative scale causal={causal}")
+
+
 FULL = [w for w in inputs.WORKLOADS if w.dtype != "e4m3"]
 
 
