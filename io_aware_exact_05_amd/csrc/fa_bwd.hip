@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -312,10 +314,13 @@ void bwd_dq(BwdParams p) {
   for (int t = 0; t < PD && t < nt; ++t) issue_tile(t, t);
   wait_vmcnt(PT * (min(PD, nt) - 1));
   __syncthreads();
-  for (int j = 0; j < nt; ++j) {
-    if (j + PD < nt) issue_tile(j + PD, (j + PD) % ST);
+  // One tile; with a compile-time ring stage SG (the loop below is unrolled
+  // over the stages) every LDS read is a register plus an immediate offset.
+  auto step = [&](int j, auto SG) __attribute__((always_inline)) {
+    const int sg = (int)SG;
+    if (j + PD < nt) issue_tile(j + PD, (sg + PD) % ST);
     if (j <= jlast) {
-      const char* sk = smem + (j % ST) * 2 * TB;
+      const char* sk = smem + sg * 2 * TB;
       const char* sv = sk + TB;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -328,23 +333,40 @@ void bwd_dq(BwdParams p) {
         // wave-uniform, so other blocks skip the selects.
         const int rel = (CAUSAL ? min(myq, N - 1) : N - 1) - key0;
         const bool hides = j * BC + kb * 32 + 31 > (CAUSAL ? min(qrow0, N - 1) : N - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(s[r], c, -lse2);
         if (hides) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-            s[r] = (16 * (r >> 3) + (r & 7) <= rel) ? pr : 0.f;
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+          for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) <= rel) ? s[r] : kNegInf;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dl);
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r]) * (dp[r] - dl);
         mm_tr<T, D>(sk + kb * 32 * RB, G, s, acc);
       }
     }
     wait_vmcnt(PT * max(0, min(j + PD, nt - 1) - (j + 1)));
     __syncthreads();
+  };
+#ifndef FA_BWD_DQ_UNROLL
+#define FA_BWD_DQ_UNROLL 1
+#endif
+  if constexpr (FA_BWD_DQ_UNROLL && D <= 128) {
+    static_assert(ST >= 2 && ST <= 4, "the unrolled loop covers rings of 2 to 4 stages");
+    for (int j = 0; j < nt; j += ST) {
+      step(j, std::integral_constant<int, 0>());
+      if (j + 1 >= nt) break;
+      step(j + 1, std::integral_constant<int, 1>());
+      if constexpr (ST > 2) {
+        if (j + 2 >= nt) break;
+        step(j + 2, std::integral_constant<int, 2 % ST>());
+        if constexpr (ST > 3) {
+          if (j + 3 >= nt) break;
+          step(j + 3, std::integral_constant<int, 3 % ST>());
+        }
+      }
+    }
+  } else {
+    for (int j = 0; j < nt; ++j) step(j, j % ST);
   }
   if (myq < N) store_row<T, D>((T*)p.dq + head + (size_t)myq * D, acc, p.scale, g);
 }
@@ -460,8 +482,17 @@ void bwd_dkdv(BwdParams p) {
   for (int t = 0; t < PD && t < ntile; ++t) issue_tile(t, t);
   wait_vmcnt(PT * (min(PD, ntile) - 1));
   __syncthreads();
-  for (int j = 0; j < ntile; ++j) {
-    if (j + PD < ntile) issue_tile(j + PD, (j + PD) % ST);
+  // One tile; the ring stage SG is a compile-time constant (the loop below is
+  // unrolled over the stages), so every LDS read is a register plus an
+  // immediate offset.
+  // DIAG: the causal selects run only on blocks that cross the diagonal (a
+  // wave-uniform branch).  At d = 128 that branch pushes the causal kernel,
+  // already at 256 registers, into spills inside the loop, so there every
+  // block takes the selects.
+  constexpr bool DIAG = D != 128;
+  auto step = [&](int j, auto SG) __attribute__((always_inline)) {
+    const int sg = (int)SG;
+    if (j + PD < ntile) issue_tile(j + PD, (sg + PD) % ST);
     const int q0 = (qs + j % cnt) * BQ;
     // Causal: skip a tile whose every query precedes every key of this wave
     // (the mask would zero it).  Not at d = 256, where the branch around the
@@ -469,7 +500,7 @@ void bwd_dkdv(BwdParams p) {
     // masked tiles are computed and contribute zero there.
     constexpr bool SKIP = CAUSAL && D != 256;
     if (!SKIP || q0 + BQ - 1 >= k0) {
-      const char* sq = smem + (j % ST) * STB;
+      const char* sq = smem + sg * STB;
       const char* sd = sq + TB;
       const float* sst = (const float*)(sq + 2 * TB);
 #pragma unroll
@@ -490,14 +521,19 @@ void bwd_dkdv(BwdParams p) {
           dd[8 * hh + 0] = b0.x; dd[8 * hh + 1] = b0.y; dd[8 * hh + 2] = b0.z; dd[8 * hh + 3] = b0.w;
           dd[8 * hh + 4] = b1.x; dd[8 * hh + 5] = b1.y; dd[8 * hh + 6] = b1.z; dd[8 * hh + 7] = b1.w;
         }
-        // causal: visible iff 16 (r/8) + r%8 >= lo (one select per score: a
-        // branch around the selects costs this kernel's register allocation
-        // spills at d = 128)
-        const int lo = mykey - (q0 + 32 * qb + 8 * g);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(s[r], c, -l2[r]);
+        // Causal: only a block some of whose queries precede some key of the
+        // wave hides pairs (query < key); the test is wave-uniform, so every
+        // other block skips the selects.  Visible iff 16 (r/8) + r%8 >= lo.
+        if (CAUSAL && (!DIAG || q0 + 32 * qb < k0 + 31)) {
+          const int lo = mykey - (q0 + 32 * qb + 8 * g);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) >= lo) ? s[r] : kNegInf;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
-          if (CAUSAL) pr = (16 * (r >> 3) + (r & 7) >= lo) ? pr : 0.f;
+          const float pr = __builtin_amdgcn_exp2f(s[r]);
           s[r] = pr;
           dp[r] = pr * (dp[r] - dd[r]);
         }
@@ -507,6 +543,21 @@ void bwd_dkdv(BwdParams p) {
     }
     wait_vmcnt(PT * max(0, min(j + PD, ntile - 1) - (j + 1)));
     __syncthreads();
+  };
+#ifndef FA_BWD_KV_UNROLL
+#define FA_BWD_KV_UNROLL 1
+#endif
+#ifndef FA_BWD_KV_UNROLL_CAUSAL
+#define FA_BWD_KV_UNROLL_CAUSAL 1
+#endif
+  constexpr bool UNROLL = D <= 128 && ST == 2 && (CAUSAL ? FA_BWD_KV_UNROLL_CAUSAL : FA_BWD_KV_UNROLL);
+  if constexpr (UNROLL) {
+    for (int j = 0; j < ntile; j += 2) {
+      step(j, std::integral_constant<int, 0>());
+      if (j + 1 < ntile) step(j + 1, std::integral_constant<int, 1>());
+    }
+  } else {
+    for (int j = 0; j < ntile; ++j) step(j, j % ST);
   }
   if (mykey < N) {
     store_row<T, D>((T*)p.dk + kvhead + (size_t)mykey * D, acck, p.scale, g);
