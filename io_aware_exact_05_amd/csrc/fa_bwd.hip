@@ -116,12 +116,15 @@ template <int D> struct Geom {
 // MFMA reads tile row swap_bits23(i)), B = 32 rows held in registers (lane
 // l: row l%32, columns 16 s + 8 g .. +8).  Register r of half-wave g of the
 // result is tile row 16 (r/8) + 8 g + r%8, column l%32.
-template <typename T, int D>
+template <typename T, int D, bool PIN>
 __device__ __forceinline__ f32x16 mm_rows(const char* blk, const Geom<D>& G,
                                           const i32x4 (&b)[D / 16]) {
   // Operands are read PF steps ahead of their MFMA: enough to cover LDS
   // latency, few enough that two of these in flight do not crowd out the
-  // accumulators at d = 256.
+  // accumulators at d = 256.  With PIN, scheduling barriers keep the reads
+  // ahead (left alone, the compiler may move each read next to its MFMA and
+  // wait for it there); without, the register allocator has the last word
+  // (bwd_dkdv at d = 128 and 256 spills with the barriers).
   constexpr int NS = D / 16, PF = NS < 4 ? NS : 4;
   f32x16 c;
 #pragma unroll
@@ -132,6 +135,7 @@ __device__ __forceinline__ f32x16 mm_rows(const char* blk, const Geom<D>& G,
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     if (s + PF < NS) a[s + PF] = *(const i32x4*)(blk + G.roff + (((2 * (s + PF)) ^ G.ry) << 4));
+    if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
     c = Half<T>::mfma(a[s], b[s], c);
   }
   return c;
@@ -139,18 +143,27 @@ __device__ __forceinline__ f32x16 mm_rows(const char* blk, const Geom<D>& G,
 
 // mm_rows with B read from LDS as well: row boff of a tile (lane l%32's
 // row), chunk (2 s + g) ^ by.
-template <typename T, int D>
+template <typename T, int D, bool PIN>
 __device__ __forceinline__ f32x16 mm_rows_lds(const char* blk, const Geom<D>& G, const char* bt,
                                               int boff, int by) {
   constexpr int NS = D / 16;
   f32x16 c;
 #pragma unroll
   for (int r = 0; r < 16; ++r) c[r] = 0.f;
+  // operands of step s + 1 are read before the MFMA of step s
+  auto rd = [&](int s, i32x4& a, i32x4& b) __attribute__((always_inline)) {
+    a = *(const i32x4*)(blk + G.roff + (((2 * s) ^ G.ry) << 4));
+    b = *(const i32x4*)(bt + boff + (((2 * s) ^ by) << 4));
+  };
+  i32x4 a0, b0, a1, b1;
+  rd(0, a0, b0);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const i32x4 a = *(const i32x4*)(blk + G.roff + (((2 * s) ^ G.ry) << 4));
-    const i32x4 b = *(const i32x4*)(bt + boff + (((2 * s) ^ by) << 4));
-    c = Half<T>::mfma(a, b, c);
+    if (s + 1 < NS) rd(s + 1, a1, b1);
+    if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+    c = Half<T>::mfma(a0, b0, c);
+    a0 = a1;
+    b0 = b1;
   }
   return c;
 }
@@ -212,6 +225,17 @@ __device__ __forceinline__ float hi16(int x, bool bf) {
   return bf ? __builtin_bit_cast(float, (unsigned)h << 16) : (float)__builtin_bit_cast(_Float16, h);
 }
 
+// Operands loaded into registers before the tile loop: a use the compiler
+// sees, right after the loads have been waited for.  Without it the compiler
+// takes them as still in flight at the loop head (it does not read the
+// inline-assembly wait) and puts vmcnt waits before their uses inside the
+// loop, which the hardware then applies to the tile copies in flight.
+template <int N>
+__device__ __forceinline__ void landed(const i32x4 (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(x[i]));
+}
+
 // ---------------------------------------------------------------------------
 // dQ (and the row statistics for bwd_dkdv)
 // ---------------------------------------------------------------------------
@@ -268,6 +292,8 @@ void bwd_dq(BwdParams p) {
   // Drain this wave's own loads and stores: the tile copies below are counted
   // on the same vmcnt and the waits in the loop count only those.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  landed(qop);
+  landed(dop);
 
   const int kv_end = CAUSAL ? min(N, (qt + 1) * BR) : N;
   const int nt = (kv_end + BC - 1) / BC;
@@ -324,8 +350,8 @@ void bwd_dq(BwdParams p) {
       const char* sv = sk + TB;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        f32x16 s = mm_rows<T, D>(sk + kb * 32 * RB, G, qop);
-        const f32x16 dp = mm_rows<T, D>(sv + kb * 32 * RB, G, dop);
+        f32x16 s = mm_rows<T, D, true>(sk + kb * 32 * RB, G, qop);
+        const f32x16 dp = mm_rows<T, D, true>(sv + kb * 32 * RB, G, dop);
         // register r holds key key0 + 16 (r/8) + r%8
         const int key0 = j * BC + kb * 32 + 8 * g;
         // visible iff 16 (r/8) + r%8 <= rel.  Only blocks that reach past N
@@ -430,6 +456,8 @@ void bwd_dkdv(BwdParams p) {
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  landed(kop);
+  if constexpr (!VLDS) landed(vop);
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qs = CAUSAL ? (kblk * BK) / BQ : 0;  // first query tile that sees a key of the block
@@ -490,6 +518,9 @@ void bwd_dkdv(BwdParams p) {
   // already at 256 registers, into spills inside the loop, so there every
   // block takes the selects.
   constexpr bool DIAG = D != 128;
+  // Operand reads held ahead of their MFMAs by scheduling barriers (at
+  // d = 128 and 256 the barriers cost this kernel spills).
+  constexpr bool PIN = D == 64;
   auto step = [&](int j, auto SG) __attribute__((always_inline)) {
     const int sg = (int)SG;
     if (j + PD < ntile) issue_tile(j + PD, (sg + PD) % ST);
@@ -505,10 +536,10 @@ void bwd_dkdv(BwdParams p) {
       const float* sst = (const float*)(sq + 2 * TB);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        f32x16 s = mm_rows<T, D>(sq + qb * 32 * RB, G, kop);
+        f32x16 s = mm_rows<T, D, PIN>(sq + qb * 32 * RB, G, kop);
         f32x16 dp;
-        if constexpr (VLDS) dp = mm_rows_lds<T, D>(sd + qb * 32 * RB, G, vlds, vboff, vby);
-        else dp = mm_rows<T, D>(sd + qb * 32 * RB, G, vop);
+        if constexpr (VLDS) dp = mm_rows_lds<T, D, PIN>(sd + qb * 32 * RB, G, vlds, vboff, vby);
+        else dp = mm_rows<T, D, PIN>(sd + qb * 32 * RB, G, vop);
         // register r holds query q0 + 32 qb + 16 (r/8) + 8 g + r%8
         float l2[16], dd[16];
 #pragma unroll
