@@ -39,14 +39,23 @@ __device__ __forceinline__ f32x16 mfma8_sab(i32x8 a, i32x8 b, f32x16 c, int sa, 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
+// Two values -> the low two bytes of a word; the high half is whatever the
+// destination register held (the builtin's form takes that half as an
+// operand, and the compiler clears a register for it).
+__device__ __forceinline__ int cvt_pk_e4m3_lo(float a, float b) {
+  int w;
+  asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(w) : "v"(a), "v"(b));
+  return w;
+}
+
+// The second conversion overwrites the high half the first one left undefined.
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, cvt_pk_e4m3_lo(a, b), true);
 }
 
 // x rounded to e4m3 (the conversion that packs P~), returned as fp32
 __device__ __forceinline__ float round_e4m3(float x) {
-  return __builtin_amdgcn_cvt_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false), 0);
+  return __builtin_amdgcn_cvt_f32_fp8(cvt_pk_e4m3_lo(x, x), 0);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {

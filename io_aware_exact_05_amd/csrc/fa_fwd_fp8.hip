@@ -272,25 +272,32 @@ void fwd_fp8(Fp8Params p) {
   };
 
   // ---- O^T += V8^T P~^T for the tile in stage st, V scale sa, P~ scale sb ----
+  // The V^T operand of each MFMA is read one MFMA ahead (its four transposed
+  // reads are in flight while the previous product runs).
   auto pv = [&](int st, const i32x8 (&P)[NKS], int sa, int sb) __attribute__((always_inline)) {
     const char* sv = smem + st * SB + TB;
+    auto vread = [&](int i) __attribute__((always_inline)) {
+      const int ks = i / ND, b = i % ND;
+      i32x2 part[4];
+#pragma unroll
+      for (int kbh = 0; kbh < 2; ++kbh)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const char* a = sv + (32 * (2 * ks + kbh) + 16 * h) * RB + vrow_off + (((2 * b) ^ vx) << 4);
+          part[2 * kbh + h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
+        }
+      return i32x8{part[0][0], part[0][1], part[1][0], part[1][1],
+                   part[2][0], part[2][1], part[3][0], part[3][1]};
+    };
     __builtin_amdgcn_s_setprio(1);
+    i32x8 va = vread(0);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int b = 0; b < ND; ++b) {
-        i32x2 part[4];
-#pragma unroll
-        for (int kbh = 0; kbh < 2; ++kbh)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const char* a = sv + (32 * (2 * ks + kbh) + 16 * h) * RB + vrow_off + (((2 * b) ^ vx) << 4);
-            part[2 * kbh + h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
-          }
-        const i32x8 va = {part[0][0], part[0][1], part[1][0], part[1][1],
-                          part[2][0], part[2][1], part[3][0], part[3][1]};
-        oacc[b] = mfma8_sab(va, P[ks], oacc[b], sa, sb);
-      }
+    for (int i = 0; i < NKS * ND; ++i) {
+      const i32x8 vn = i + 1 < NKS * ND ? vread(i + 1) : va;
+      __builtin_amdgcn_sched_barrier(0);  // keep the next reads ahead of this MFMA
+      oacc[i % ND] = mfma8_sab(va, P[i / ND], oacc[i % ND], sa, sb);
+      va = vn;
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
