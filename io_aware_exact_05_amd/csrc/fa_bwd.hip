@@ -225,17 +225,6 @@ __device__ __forceinline__ float hi16(int x, bool bf) {
   return bf ? __builtin_bit_cast(float, (unsigned)h << 16) : (float)__builtin_bit_cast(_Float16, h);
 }
 
-// Operands loaded into registers before the tile loop: a use the compiler
-// sees, right after the loads have been waited for.  Without it the compiler
-// takes them as still in flight at the loop head (it does not read the
-// inline-assembly wait) and puts vmcnt waits before their uses inside the
-// loop, which the hardware then applies to the tile copies in flight.
-template <int N>
-__device__ __forceinline__ void landed(const i32x4 (&x)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(x[i]));
-}
-
 // ---------------------------------------------------------------------------
 // dQ (and the row statistics for bwd_dkdv)
 // ---------------------------------------------------------------------------

@@ -87,6 +87,7 @@ void decode_partial(DecodeParams p) {
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  landed(qop);
   const float c = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
   // last key this lane's query may see
   const int lim = CAUSAL ? Nkv - p.Nq + (min(rho, p.R - 1) % p.Nq) : Nkv - 1;

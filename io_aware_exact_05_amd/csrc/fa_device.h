@@ -50,6 +50,17 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
                : "memory", "m0");
 }
 
+// Operands loaded into registers before a tile loop: a use the compiler
+// sees, right after the loads have been waited for.  Without it the compiler
+// takes them as still in flight at the loop head (it does not read an
+// inline-assembly wait) and puts vmcnt waits before their uses inside the
+// loop, which the hardware then applies to the tile copies in flight.
+template <int N>
+__device__ __forceinline__ void landed(const i32x4 (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(x[i]));
+}
+
 // Raw buffer resource over [base, base + bytes) (stride 0; data format 32 bit,
 // the value the gfx9 family expects for untyped buffer loads).
 // The base address and size go through readfirstlane: the resource must
