@@ -46,12 +46,14 @@ constexpr int kBwdNW = 4;  // waves per workgroup (32 rows or keys each)
 // BC: key rows per bwd_dq tile; BQ: query rows per bwd_dkdv tile; OCC: waves
 // per SIMD the register budget of each kernel is cut to; ST_*: LDS ring
 // stages of each kernel (tiles are prefetched ST - 1 ahead).  At d = 128,
-// bwd_dq streams 32-key tiles through a 4-stage ring (the same 64 KiB of LDS
-// as 64-key tiles in 2 stages): 5-7% faster on 2048-token heads, equal on
-// 8192-token heads; bwd_dkdv takes 32-query tiles with V in LDS at two waves
-// per SIMD (see bwd_dkdv).  At d = 64 bwd_dq fits three waves per SIMD (138
-// registers): up to 10% over two (bwd_dkdv at three, with 32-query tiles, did
-// not add to it).  The FA_BWD_* macros exist for tuning builds only.
+// bwd_dq streams 64-key tiles through a 2-stage ring (the same 64 KiB of LDS
+// as 32-key tiles in 4 stages, which had been 5-7% faster while the loop ran
+// over a run-time ring stage; with the loops unrolled over the stages the
+// 64-key tiles are 2% faster without masking, equal with it); bwd_dkdv takes
+// 32-query tiles with V in LDS at two waves per SIMD (see bwd_dkdv).  At
+// d = 64 bwd_dq fits three waves per SIMD (138 registers): up to 10% over two
+// (bwd_dkdv at three, with 32-query tiles, did not add to it).  The FA_BWD_*
+// macros exist for tuning builds only.
 #ifndef FA_BWD_D64_BC
 #define FA_BWD_D64_BC 64
 #endif
@@ -59,7 +61,7 @@ constexpr int kBwdNW = 4;  // waves per workgroup (32 rows or keys each)
 #define FA_BWD_D64_BQ 64
 #endif
 #ifndef FA_BWD_D128_BC
-#define FA_BWD_D128_BC 32
+#define FA_BWD_D128_BC 64
 #endif
 #ifndef FA_BWD_D128_BQ
 #define FA_BWD_D128_BQ 32
@@ -71,7 +73,7 @@ constexpr int kBwdNW = 4;  // waves per workgroup (32 rows or keys each)
 #define FA_BWD_D64_STKV 2
 #endif
 #ifndef FA_BWD_D128_STDQ
-#define FA_BWD_D128_STDQ 4
+#define FA_BWD_D128_STDQ 2
 #endif
 #ifndef FA_BWD_D128_STKV
 #define FA_BWD_D128_STKV 2
