@@ -194,15 +194,17 @@ void fwd_pipe(FwdParams p) {
     }
   };
   set_addrs();
-  // Buffer resources over one head's rows: K and V of the current item and
-  // of the next one, O and the logsumexp of the current item.
+  // Buffer resources over one head's rows: O and the logsumexp of the
+  // current item; K and V (of the current item and of the next one) get one
+  // per copied tile, starting at the tile (see issue_k).
   const uint32_t head_bytes = (uint32_t)N * kRB;
   const T* qh;
-  __amdgpu_buffer_rsrc_t kbuf, vbuf, obuf, lbuf, kbuf_n, vbuf_n;
-  auto kv_rsrc = [&](int h, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr) __attribute__((always_inline)) {
+  __amdgpu_buffer_rsrc_t obuf, lbuf;
+  const T *kp, *vp, *kp_n, *vp_n;
+  auto kv_rsrc = [&](int h, const T*& kr, const T*& vr) __attribute__((always_inline)) {
     const size_t kvhead = (size_t)kv_head(p, h) * N * kD;
-    kr = make_rsrc((const T*)p.k + kvhead, head_bytes);
-    vr = make_rsrc((const T*)p.v + kvhead, head_bytes);
+    kr = (const T*)p.k + kvhead;
+    vr = (const T*)p.v + kvhead;
   };
   auto set_head = [&](int h) __attribute__((always_inline)) {
     const size_t head = (size_t)h * N * kD;
@@ -211,31 +213,42 @@ void fwd_pipe(FwdParams p) {
     lbuf = make_rsrc(p.lse + (size_t)h * N, (uint32_t)N * 4u);
   };
   set_head(bh);
-  kv_rsrc(bh, kbuf, vbuf);
+  kv_rsrc(bh, kp, vp);
   if constexpr (PAIR) {
-    if (has_next) kv_rsrc(bh2, kbuf_n, vbuf_n);
+    if (has_next) kv_rsrc(bh2, kp_n, vp_n);
   }
   // Tile t of the current item sits in ring stage t % ST.  Past the item's
   // last tile the copies continue with the next item's first tiles (the
   // first item's tile count is a multiple of ST, so they land in the stages
   // the next item expects), or, after the last item, read as zeros
   // (hardware range check): every barrier issues the same number of copies
-  // and the wait counts stay constant.
+  // and the wait counts stay constant.  Each tile's copies go through a
+  // resource that starts at the tile and ends with the head (empty past
+  // it), so the per-lane offsets ld_voff serve every tile unchanged: the
+  // tile's offset is scalar work, not a vector add per copy.
+  auto tile_rsrc = [&](const T* base, uint32_t t0) __attribute__((always_inline)) {
+    // Bytes left in the head past t0, saturating at 0, in scalar registers
+    // (written out: the compiler's saturating subtract is a vector one, and
+    // it would then build the resource in vector registers).
+    uint32_t left;
+    asm("s_sub_u32 %0, %1, %2\n\ts_cselect_b32 %0, 0, %0" : "=s"(left) : "s"(head_bytes), "s"(t0) : "scc");
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + t0), 0, (int)left, 0x00020000);
+  };
   auto issue_k = [&](int t) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + (uint32_t)(t % ST) * TB + w * 1024;
     const bool nx = PAIR && t >= nt && has_next;
-    const uint32_t t0 = (uint32_t)(nx ? t - nt : t) * TB;
-    const __amdgpu_buffer_rsrc_t r = nx ? kbuf_n : kbuf;
+    const uint32_t t0 = __builtin_amdgcn_readfirstlane((uint32_t)(nx ? t - nt : t) * TB);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(nx ? kp_n : kp, t0);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) buf_dma16(r, t0 + ld_voff[u], dst + u * NW * 1024);
+    for (int u = 0; u < CPT; ++u) buf_dma16(r, ld_voff[u], dst + u * NW * 1024);
   };
   auto issue_v = [&](int t) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + VBASE + (uint32_t)(t % ST) * TB + w * 1024;
     const bool nx = PAIR && t >= nt && has_next;
-    const uint32_t t0 = (uint32_t)(nx ? t - nt : t) * TB;
-    const __amdgpu_buffer_rsrc_t r = nx ? vbuf_n : vbuf;
+    const uint32_t t0 = __builtin_amdgcn_readfirstlane((uint32_t)(nx ? t - nt : t) * TB);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(nx ? vp_n : vp, t0);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) buf_dma16(r, t0 + ld_voff[u], dst + u * NW * 1024);
+    for (int u = 0; u < CPT; ++u) buf_dma16(r, ld_voff[u], dst + u * NW * 1024);
   };
 
   // LDS read geometry (as in fwd_wide): see set_addrs.
@@ -646,8 +659,8 @@ void fwd_pipe(FwdParams p) {
     if (has_next) {
       set_item(qt2);
       set_head(bh2);
-      kbuf = kbuf_n;
-      vbuf = vbuf_n;
+      kp = kp_n;
+      vp = vp_n;
       has_next = false;
       load_q(qrow0);
       q_landed();
