@@ -290,26 +290,27 @@ void bwd_dq(BwdParams p) {
   const int nt = (kv_end + BC - 1) / BC;
   const int jlast = qrow0 >= N ? -1 : CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1;
 
-  // Tile copies through buffer resources bounded by the head: key rows past
-  // N read as zeros (their scores are masked, and zero K rows add nothing to
-  // dQ), and a copy's address is a constant per-lane offset plus the tile's.
+  // Tile copies through per-tile buffer resources that end with the head:
+  // key rows past N read as zeros (their scores are masked, and zero K rows
+  // add nothing to dQ), and a copy's address is a constant per-lane offset.
   uint32_t ld_voff[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int s = (u * NW + w) * 64 + lane, row = s / CPR, c = s % CPR;
     ld_voff[u] = (uint32_t)(row * RB + (c ^ chunk_swz<D>(row)) * 16);
   }
-  const __amdgpu_buffer_rsrc_t kbuf = make_rsrc(kh, (uint32_t)N * RB);
-  const __amdgpu_buffer_rsrc_t vbuf = make_rsrc(vh, (uint32_t)N * RB);
+
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
   auto issue_tile = [&](int j, int stage) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + stage * 2 * TB;
     const uint32_t t0 = (uint32_t)j * TB;
+    const __amdgpu_buffer_rsrc_t kbuf = tile_rsrc(kh, (uint32_t)N * RB, t0);
+    const __amdgpu_buffer_rsrc_t vbuf = tile_rsrc(vh, (uint32_t)N * RB, t0);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const uint32_t lo = dst + (u * NW + w) * 1024;
-      buf_dma16(kbuf, t0 + ld_voff[u], lo);
-      buf_dma16(vbuf, t0 + ld_voff[u], lo + TB);
+      buf_dma16(kbuf, ld_voff[u], lo);
+      buf_dma16(vbuf, ld_voff[u], lo + TB);
     }
   };
 
@@ -455,8 +456,9 @@ void bwd_dkdv(BwdParams p) {
   const int cnt = nqt - qs;
   const int ntile = grp * cnt;
 
-  // Q and dO tiles through buffer resources bounded by the query head:
-  // rows past N read as zeros (their base-2 lse is +inf, so P = 0 there).
+  // Q and dO tiles through per-tile buffer resources that end with the query
+  // head: rows past N read as zeros (their base-2 lse is +inf, so P = 0
+  // there).
   uint32_t ld_voff[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
@@ -473,15 +475,14 @@ void bwd_dkdv(BwdParams p) {
     const int hh = j / cnt, qt = qs + j % cnt;
     const int bhq = qh0 + hh;
     const size_t hq = (size_t)bhq * N * D;
-    const __amdgpu_buffer_rsrc_t qbuf = make_rsrc((const T*)p.q + hq, (uint32_t)N * RB);
-    const __amdgpu_buffer_rsrc_t dbuf = make_rsrc((const T*)p.dout + hq, (uint32_t)N * RB);
+    const __amdgpu_buffer_rsrc_t qbuf = tile_rsrc((const T*)p.q + hq, (uint32_t)N * RB, (uint32_t)qt * TB);
+    const __amdgpu_buffer_rsrc_t dbuf = tile_rsrc((const T*)p.dout + hq, (uint32_t)N * RB, (uint32_t)qt * TB);
     const uint32_t dst = smem_base + stage * STB;
-    const uint32_t t0 = (uint32_t)qt * TB;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const uint32_t lo = dst + (u * NW + w) * 1024;
-      buf_dma16(qbuf, t0 + ld_voff[u], lo);
-      buf_dma16(dbuf, t0 + ld_voff[u], lo + TB);
+      buf_dma16(qbuf, ld_voff[u], lo);
+      buf_dma16(dbuf, ld_voff[u], lo + TB);
     }
     if (lane < SL) dma16(s_src + (size_t)bhq * p.Npad + qt * BQ, dst + 2 * TB + w * SL * 16);
   };

@@ -73,6 +73,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// Raw buffer resource over [base + off, base + bytes), empty when off >= bytes,
+// built in scalar registers: the copies of a tile at byte offset off then
+// use per-lane offsets relative to the tile, and the tile offset costs no
+// vector instruction.  The saturating subtract is written out because the
+// compiler's form of it is a vector instruction (which would then put the
+// whole resource in vector registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes, uint32_t off) {
+  const uint32_t o = __builtin_amdgcn_readfirstlane(off);
+  const uint32_t b = __builtin_amdgcn_readfirstlane(bytes);
+  uint32_t left;
+  asm("s_sub_u32 %0, %1, %2\n\ts_cselect_b32 %0, 0, %0" : "=s"(left) : "s"(b), "s"(o) : "scc");
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + o), 0, (int)left, 0x00020000);
+}
+
 // 16-byte buffer -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane i's
 // bytes land at LDS address lds_addr + 16 i.  An offset past the resource's
 // size reads zeros instead of memory.  Inline assembly for the same reason

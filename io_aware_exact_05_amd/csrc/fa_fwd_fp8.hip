@@ -128,9 +128,9 @@ void fwd_fp8(Fp8Params p) {
   const int jlast = qrow0 >= N ? -1 : (CAUSAL ? min(nt - 1, (qrow0 + 31) / BC) : nt - 1);
 
   // ---- copies (as in the 16-bit kernel, D-byte rows) ----
-  // Buffer resources bounded by the head: rows past N read as zeros (their
-  // keys are masked), and a copy's address is a constant per-lane offset
-  // plus the tile's wave-uniform one.
+  // Per tile, buffer resources from the tile to the end of the head: rows
+  // past N read as zeros (their keys are masked), and a copy's address is a
+  // constant per-lane offset.
   uint32_t ld_voff[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
@@ -138,16 +138,16 @@ void fwd_fp8(Fp8Params p) {
     ld_voff[u] = (uint32_t)(row * RB + (ch16 ^ swz8<D>(row)) * 16);
   }
   const uint32_t head_bytes = (uint32_t)N * RB;
-  const __amdgpu_buffer_rsrc_t kbuf = make_rsrc(kh, head_bytes);
-  const __amdgpu_buffer_rsrc_t vbuf = make_rsrc(vh, head_bytes);
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
   auto issue_tile = [&](int j) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + (j % ST) * SB + w * 1024;
     const uint32_t t0 = (uint32_t)j * TB;
+    const __amdgpu_buffer_rsrc_t kbuf = tile_rsrc(kh, head_bytes, t0);
+    const __amdgpu_buffer_rsrc_t vbuf = tile_rsrc(vh, head_bytes, t0);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      buf_dma16(kbuf, t0 + ld_voff[u], dst + u * NW * 1024);
-      buf_dma16(vbuf, t0 + ld_voff[u], dst + u * NW * 1024 + TB);
+      buf_dma16(kbuf, ld_voff[u], dst + u * NW * 1024);
+      buf_dma16(vbuf, ld_voff[u], dst + u * NW * 1024 + TB);
     }
   };
 

@@ -226,27 +226,19 @@ void fwd_pipe(FwdParams p) {
   // resource that starts at the tile and ends with the head (empty past
   // it), so the per-lane offsets ld_voff serve every tile unchanged: the
   // tile's offset is scalar work, not a vector add per copy.
-  auto tile_rsrc = [&](const T* base, uint32_t t0) __attribute__((always_inline)) {
-    // Bytes left in the head past t0, saturating at 0, in scalar registers
-    // (written out: the compiler's saturating subtract is a vector one, and
-    // it would then build the resource in vector registers).
-    uint32_t left;
-    asm("s_sub_u32 %0, %1, %2\n\ts_cselect_b32 %0, 0, %0" : "=s"(left) : "s"(head_bytes), "s"(t0) : "scc");
-    return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + t0), 0, (int)left, 0x00020000);
-  };
   auto issue_k = [&](int t) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + (uint32_t)(t % ST) * TB + w * 1024;
     const bool nx = PAIR && t >= nt && has_next;
-    const uint32_t t0 = __builtin_amdgcn_readfirstlane((uint32_t)(nx ? t - nt : t) * TB);
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(nx ? kp_n : kp, t0);
+    const uint32_t t0 = (uint32_t)(nx ? t - nt : t) * TB;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(nx ? kp_n : kp, head_bytes, t0);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) buf_dma16(r, ld_voff[u], dst + u * NW * 1024);
   };
   auto issue_v = [&](int t) __attribute__((always_inline)) {
     const uint32_t dst = smem_base + VBASE + (uint32_t)(t % ST) * TB + w * 1024;
     const bool nx = PAIR && t >= nt && has_next;
-    const uint32_t t0 = __builtin_amdgcn_readfirstlane((uint32_t)(nx ? t - nt : t) * TB);
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(nx ? vp_n : vp, t0);
+    const uint32_t t0 = (uint32_t)(nx ? t - nt : t) * TB;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(nx ? vp_n : vp, head_bytes, t0);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) buf_dma16(r, ld_voff[u], dst + u * NW * 1024);
   };

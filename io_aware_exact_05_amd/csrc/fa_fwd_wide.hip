@@ -140,9 +140,10 @@ void fwd_wide(FwdParams p) {
   const int jlast = qrow0 >= N ? -1 : (CAUSAL ? min(nt - 1, (qrow0 + WR - 1) / BC) : nt - 1);
 
   // ---- tile copies: wave w, instruction u fills slots (u NW + w) 64 + lane ----
-  // Buffer loads against a resource that spans exactly this head's K (or V):
-  // rows past N fail the hardware range check and read as zeros, and the
-  // per-tile offset is one add.
+  // Buffer loads against a resource from the tile to the end of this head's
+  // K (or V), built per tile in scalar registers: rows past N fail the
+  // hardware range check and read as zeros, and a copy's address is a
+  // constant per-lane offset.
   uint32_t ld_voff[CPT];  // byte offset of this lane's chunk within a tile
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
@@ -150,16 +151,16 @@ void fwd_wide(FwdParams p) {
     ld_voff[u] = row * RB + (ch ^ chunk_swz<D>(row)) * 16;
   }
   const uint32_t head_bytes = (uint32_t)N * RB;
-  const __amdgpu_buffer_rsrc_t kbuf = make_rsrc(kh, head_bytes);
-  const __amdgpu_buffer_rsrc_t vbuf = make_rsrc(vh, head_bytes);
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
   auto issue_tile = [&](int j) __attribute__((always_inline)) {
     const uint32_t kdst = smem_base + (j % ST) * 2 * TB + w * 1024;
     const uint32_t t0 = (uint32_t)j * TB;
+    const __amdgpu_buffer_rsrc_t kbuf = tile_rsrc(kh, head_bytes, t0);
+    const __amdgpu_buffer_rsrc_t vbuf = tile_rsrc(vh, head_bytes, t0);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      buf_dma16(kbuf, t0 + ld_voff[u], kdst + u * NW * 1024);
-      buf_dma16(vbuf, t0 + ld_voff[u], kdst + u * NW * 1024 + TB);
+      buf_dma16(kbuf, ld_voff[u], kdst + u * NW * 1024);
+      buf_dma16(vbuf, ld_voff[u], kdst + u * NW * 1024 + TB);
     }
   };
 
