@@ -19,11 +19,13 @@ SOURCES = ["api.cpp", "fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_pipe.hip", "fa_fw
            "fa_quant.hip", "fa_bwd.hip", "fa_decode.hip"]
 # Extra flags per source.  fa_fwd_wide.hip and fa_fwd_pipe.hip keep their
 # MFMA accumulators in VGPRs (VGPR form): their registers then fit two waves
-# per SIMD with no copies between the VGPR and AGPR files.  Both also assume
-# no NaN operands, which lets a row maximum be v_max3_f32 chains without
-# canonicalising every MFMA result first (fwd_wide: 1-2% at d = 256).
+# per SIMD with no copies between the VGPR and AGPR files.  The forward
+# kernels also assume no NaN operands, which lets a row maximum be v_max3_f32
+# chains without canonicalising every MFMA result first (fwd_wide: 1-2% at
+# d = 256).
 SOURCE_FLAGS = {"fa_fwd_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-                "fa_fwd_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
+                "fa_fwd_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+                "fa_fwd_fp8.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled: hipcc -O3 would otherwise form

@@ -241,14 +241,14 @@ void fwd_fp8(Fp8Params p) {
     sb = 127 + isig - 8;
     const float beta = (8.0f - sig) + __builtin_amdgcn_logf(f) - m;
     const float lsc = __builtin_amdgcn_ldexpf(__builtin_amdgcn_rcpf(f), isig - 8);
-    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs4[4];  // four partial row sums; the first four P start them
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], ct, beta));
         S[kb][r] = pr;
-        rs4[r & 3] += pr;
+        rs4[r & 3] = (kb == 0 && r < 4) ? pr : rs4[r & 3] + pr;
       }
     l += ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3])) * lsc;
     // the row's largest P~ of this tile (0 if all keys are hidden)
