@@ -58,13 +58,17 @@ def test_small_shapes_every_element(dtype, d, N, causal):
         assert st["o_max_abs"] < 1e-4 and st["lse_max_abs"] < 1e-4, st
 
 
-# Kernel routing: d = 128 always runs fwd_pipe (256-row workgroups).  At
-# d = 64 and 256, causal launches whose grid fits in one round of fwd_wide's
-# workgroup slots (one 512-row workgroup per CU at d = 64, one 256-row one at
-# d = 256) go to the 8-wave 32-row fwd_mfma16, all others to fwd_wide.  The
+# Kernel routing: d = 128 always runs fwd_pipe (256-row workgroups).  With
+# causal masking at d = 64, a launch with at least two rounds of 512-row
+# workgroups (one per CU) runs fwd_wide's long-causal configuration (64 rows
+# per wave, ping-pong halves); otherwise, at d = 64 and 256, a launch whose
+# grid exceeds one round of fwd_wide's causal slots (d = 64: 128-row
+# workgroups, three per CU; d = 256: 256-row workgroups, one per CU) runs
+# fwd_wide, and one that fits in a round the 8-wave 32-row fwd_mfma16.  The
 # small shapes above take the fwd_mfma16 route for causal masking at d = 64
 # and 256; these head counts push small, ragged causal launches onto the
-# other kernels, element by element.
+# other kernels, element by element (BH = 800, N = 100 at d = 64 reaches the
+# long-causal configuration, the others the 128-row one).
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("BH,N", [(800, 100), (400, 300), (260, 257)])
