@@ -159,6 +159,48 @@ def test_fp8_kernel_on_oracle_quantised_inputs(d, N, causal, rotate):
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("N", [300, 1000])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_fp8_kernel_descales_not_powers_of_two(d, N, causal):
+    """The kernel with caller-supplied descales that are not powers of two
+    (this library's quantiser only writes powers of two).  A V descale
+    2^e f with f in (1/2, 1) puts log2 f into the exponent of P~ and 1/f
+    into the row sum; Q and K descales enter the score scale.  Codes come
+    from the oracle's quantiser, every descale is then replaced by a random
+    value in [0.002, 0.05), and the fp64 oracle runs on the values the codes
+    and those descales stand for, under the kernel-alone bounds."""
+    _say(f"case fp8 kernel arbitrary descales d={d} N={N} causal={causal}")
+    fa = _fa()
+    B, H = 1, 2
+    q, k, v = _fp32_inputs(B, H, N, d, seed=N + 5 * d + causal)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    rng = np.random.default_rng(N + d)
+    codes, descs = [], []
+    for x in (q, k, v):
+        c, ds = qo.quantize_blocks(x.numpy(), 128)
+        codes.append(c)
+        descs.append(rng.uniform(0.002, 0.05, ds.shape).astype(np.float32))
+    mant = np.frexp(descs[2])[0]
+    assert (mant != 0.5).all()  # no power of two among the V descales
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), device="cuda")
+    fa.fa_fwd_fp8(*(dev(c) for c in codes), *(dev(ds) for ds in descs), o, lse, bool(causal), scale)
+    torch.cuda.synchronize()
+    Qd, Kd, Vd = (qo.dequantize_blocks(c, ds) for c, ds in zip(codes, descs))
+    o_ref, lse_ref = oracle.attention(Qd, Kd, Vd, causal, scale)
+    o_np, lse_np = widen(o.cpu()), widen(lse.cpu())
+    assert np.isfinite(o_np).all() and np.isfinite(lse_np).all()
+    o_tol, lse_tol = _fp8_kernel_bounds(Qd, Kd, Vd, causal, scale, o_ref, lse_ref)
+    err = _rel_rmse(o_np, o_ref)
+    ro = float((np.abs(o_np - o_ref) / o_tol).max())
+    rl = float((np.abs(lse_np - lse_ref) / lse_tol).max())
+    _say(f"  rel-RMSE {err:.5f}  worst |dO|/bound {ro:.3f}  worst |dLSE|/bound {rl:.3f}")
+    assert err <= KERNEL_REL_RMSE
+    assert ro <= 1.0 and rl <= 1.0
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_fp8_attention_exactly_representable_inputs(d, causal):
     """Values in {0, +-1/2, +-1} with one 8 per block and column are quantised
