@@ -202,6 +202,38 @@ def test_fp8_kernel_descales_not_powers_of_two(d, N, causal):
 
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_fp8_kernel_negative_and_zero_scale(d, causal, scale):
+    """A negative softmax scale reaches the kernel as Q codes with flipped
+    sign bits and |scale|; a zero scale makes every visible key's weight
+    equal (O the mean of the visible V rows, LSE the log of their count).
+    Oracle-quantised inputs, N = 300 (a ragged third block), kernel-alone
+    bounds."""
+    _say(f"case fp8 kernel scale={scale} d={d} causal={causal}")
+    fa = _fa()
+    B, H, N = 1, 2, 300
+    q, k, v = _fp32_inputs(B, H, N, d, seed=17 * d + causal)
+    cq, dq = qo.quantize_blocks(q.numpy(), 128)
+    ck, dk = qo.quantize_blocks(k.numpy(), 128)
+    cv, dv = qo.quantize_blocks(v.numpy(), 128)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), device="cuda")
+    fa.fa_fwd_fp8(dev(cq), dev(ck), dev(cv), dev(dq), dev(dk), dev(dv), o, lse, bool(causal), scale)
+    torch.cuda.synchronize()
+    Qd, Kd, Vd = (qo.dequantize_blocks(c, ds) for c, ds in ((cq, dq), (ck, dk), (cv, dv)))
+    o_ref, lse_ref = oracle.attention(Qd, Kd, Vd, causal, scale)
+    o_np, lse_np = widen(o.cpu()), widen(lse.cpu())
+    assert np.isfinite(o_np).all() and np.isfinite(lse_np).all()
+    o_tol, lse_tol = _fp8_kernel_bounds(Qd, Kd, Vd, causal, scale, o_ref, lse_ref)
+    ro = float((np.abs(o_np - o_ref) / o_tol).max())
+    rl = float((np.abs(lse_np - lse_ref) / lse_tol).max())
+    _say(f"  worst |dO|/bound {ro:.3f}  worst |dLSE|/bound {rl:.3f}")
+    assert ro <= 1.0 and rl <= 1.0
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [0, 1])
 def test_fp8_attention_exactly_representable_inputs(d, causal):
     """Values in {0, +-1/2, +-1} with one 8 per block and column are quantised
     without error (the descale 2^-5 maps them onto the e4m3 codes of 0, 16,
